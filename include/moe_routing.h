@@ -1,0 +1,209 @@
+/*
+ * moe_routing.h — C ABI of the MoE routing-and-combine hot path on MI355X
+ * (gfx950).
+ *
+ * The four calls, in pipeline order:
+ *
+ *   moe_route             router projection, sigmoid + bias selection, sorted
+ *                         top-k with lowest-id ties, renormalised weights,
+ *                         per-token validity mask
+ *   moe_dispatch          expert histogram, exclusive prefix scan, stable
+ *                         permutation of the routed slots by expert
+ *   moe_norm_quant_nvfp4  RMSNorm of the expert input with one BF16 rounding,
+ *                         fused with NVFP4 quantisation (E2M1 codes, E4M3
+ *                         block-16 scales, static global scale)
+ *   moe_combine           per-row RMSNorm of each selected expert output,
+ *                         routing-weight scaling and top-k sum; invalid slots
+ *                         are never read
+ *
+ * Conventions shared by every call:
+ *   - Every array argument is a DEVICE pointer (memory the caller allocated on
+ *     the current HIP device), row-major, contiguous and 16-byte aligned
+ *     (MOE_ERR_ALIGN otherwise). The caller owns all
+ *     memory; the library never allocates, frees or synchronises, and keeps no
+ *     state between calls.
+ *   - `stream` is the caller's hipStream_t (NULL = the null stream). Work is
+ *     enqueued on it; the call returns without waiting.
+ *   - The return value is MOE_OK (0) or a negative MOE_ERR_* status. Every
+ *     argument check runs before any work is enqueued, so a failing call
+ *     leaves every output untouched. MOE_ERR_HIP reports a failed launch.
+ *   - BF16 values are passed as their uint16_t bit patterns.
+ *   - T == 0 (no tokens) is valid and enqueues nothing.
+ *   - Outputs are fully written; nothing needs clearing beforehand.
+ *   - Shapes are run-time arguments; nothing is compiled per token count.
+ */
+#ifndef MOE_ROUTING_H
+#define MOE_ROUTING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL_ARG = -1,   /* a required pointer is NULL */
+    MOE_ERR_BAD_SHAPE = -2,  /* a size is out of the supported range */
+    MOE_ERR_BAD_DTYPE = -3,  /* unknown dtype code */
+    MOE_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required */
+    MOE_ERR_BAD_ARG = -5,    /* a scalar argument is out of range (eps, scale) */
+    MOE_ERR_HIP = -6,        /* the HIP runtime rejected a launch */
+    MOE_ERR_ALIGN = -7       /* an array pointer is not 16-byte aligned */
+};
+
+enum moe_dtype {
+    MOE_DTYPE_F32 = 0,
+    MOE_DTYPE_BF16 = 1
+};
+
+/* Supported ranges (checked by every call). */
+#define MOE_MAX_EXPERTS 4096
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_HIDDEN 16384
+
+/* Text for a status code (static storage; never NULL). */
+const char* moe_status_string(int status);
+
+/*
+ * moe_route — router projection and routing.
+ *
+ * Defined by TensorRT-LLM PR #21356 ("Add the Muse Spark Open decoder fast
+ * paths"), description, Triton kernels "Router projection" (FP32 weights and
+ * accumulation, input cast and scale folded in) and "Routing" (sigmoid, bias,
+ * top-k, renormalised weights; picks sorted, exact ties to the lowest id); by
+ * TensorRT-LLM PR #21042 ("Add the Muse Spark Open model"), "MoE" (the router
+ * runs in FP32); and by lmdeploy PR #4835 (MoE gate v2: a required per-token
+ * validity mask, invalid tokens produce no routing entries; the aux-loss-free
+ * gate uses the bias for selection only).
+ *
+ * For every token t and expert e:
+ *   logits[t,e] = scale * sum_i hidden[t,i] * W[e,i]      FP32 accumulation
+ *   s[t,e]      = sigmoid(logits[t,e])                    correctly rounded FP32
+ *   key[t,e]    = s[t,e] + bias[e]                        FP32
+ * topk_ids[t,:] are the k experts with the largest keys, ordered by key
+ * (largest first), equal keys by ascending expert id.
+ * topk_w[t,j]  = s[t,id_j] / (s[t,id_0] + ... + s[t,id_{k-1}])   (FP32 sum in
+ * pick order, one FP32 division).
+ * token_mask[t] == 0: topk_ids[t,:] = -1 and topk_w[t,:] = 0.0; such a token's
+ * input is never inspected (it may hold NaN).
+ *
+ * Arguments:
+ *   hidden        [T,H] in hidden_dtype (MOE_DTYPE_BF16 bits or MOE_DTYPE_F32),
+ *                 or NULL for logits-in mode: `logits` is then an INPUT [T,E]
+ *                 and the projection is skipped.
+ *   W             [E,H] FP32 router weight (nn.Linear orientation). Unused in
+ *                 logits-in mode (may be NULL).
+ *   bias          [E] FP32 selection bias (required).
+ *   token_mask    [T] u8, nonzero = valid (required).
+ *   scale         finite scale applied to the dot products (1.0 for none).
+ *   T >= 0, 1 <= H <= MOE_MAX_HIDDEN with H % 16 == 0,
+ *   1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK).
+ *   logits        [T,E] FP32: output (projection mode) or input (logits-in).
+ *                 In projection mode the rows of invalid tokens hold whatever
+ *                 their (possibly NaN) input gives.
+ *   topk_ids      [T,k] int32 output; topk_w [T,k] FP32 output.
+ *   workspace     device scratch of at least moe_route_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); 256-byte aligned.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_ARG (non-finite scale),
+ * WORKSPACE, HIP.
+ */
+size_t moe_route_workspace_bytes(int T, int H, int E, int k, int hidden_dtype, int logits_in);
+
+int moe_route(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+              const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+              float* logits, int32_t* topk_ids, float* topk_w,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch — histogram, scan and permutation of the routed slots.
+ *
+ * Defined by lmdeploy PR #4835 ("Intern-S2-Mobius meta-MoE support, MoE gate
+ * v2, CP attention fixes"): the gate's shared-memory expert histogram and
+ * hierarchical multi-block scan over tiles, the required validity mask
+ * (invalid tokens get no entry), and the slot-to-position map cleared to -1.
+ *
+ * Slot f = t*k + j is valid when 0 <= topk_ids[t,j] < E.
+ *   counts[e]     number of valid slots routed to expert e          [E]
+ *   offsets[e]    exclusive prefix sum of counts; offsets[E] = valid slots
+ *                                                                    [E+1]
+ *   perm[p]       flat slot at position p: slots grouped by ascending expert,
+ *                 ascending flat index within an expert (stable); -1 for
+ *                 p >= offsets[E]                                    [T*k]
+ *   dest[f]       position of slot f, or -1 if slot f is not valid   [T*k]
+ * All outputs int32 and fully written. T >= 0, 1 <= k <= MOE_MAX_TOPK,
+ * 1 <= E <= MOE_MAX_EXPERTS, T*k < 2^31. The result is deterministic.
+ * workspace: at least moe_dispatch_workspace_bytes(T, k, E) bytes.
+ * Errors: NULL_ARG, BAD_SHAPE, WORKSPACE, HIP.
+ */
+size_t moe_dispatch_workspace_bytes(int T, int k, int E);
+
+int moe_dispatch(const int32_t* topk_ids, int T, int k, int E,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_norm_quant_nvfp4 — RMSNorm + NVFP4 quantisation of the expert input.
+ *
+ * Defined by the vLLM API docs of vllm.models.muse_spark.nvidia.ops.
+ * prepare_trtllm_nvfp4 (`norm_quant_trtllm_nvfp4` and the block quantizer
+ * `_quantize_nvfp4_global_scale`) and TensorRT-LLM PR #21356, "Numerics" (the
+ * gain centre is added to the weight in FP32, the norm rounds only its
+ * result to BF16).
+ *
+ * Per row t:  g_i = gain_center + norm_w[i]                  FP32
+ *             y_i = bf16( x_i * g_i / sqrt(mean_i(x_i^2) + eps) )
+ * Per block of 16 consecutive y (all FP32 steps, IEEE-rounded reciprocals):
+ *             sf   = e4m3_satfinite( gs * (amax|y| * (1/6)) )
+ *             out  = sf != 0 ? 1 / (sf * (1/gs)) : 0
+ *             code = e2m1_rne_saturating(y * out), bit 3 set when y*out < 0
+ * packed[t, i/2] holds code(2m) in its low nibble and code(2m+1) in its high
+ * nibble; scales[t, b] is the E4M3 byte of block b (linear layout).
+ *
+ *   x            [T,H] BF16 bits.   norm_w [H] FP32.
+ *   gain_center  finite FP32.       eps >= 0, finite (0 allowed).
+ *   global_scale device pointer to ONE FP32 value gs > 0 (static scale).
+ *   T >= 0, 16 <= H <= MOE_MAX_HIDDEN, H % 16 == 0.
+ *   packed [T, H/2] u8 output; scales [T, H/16] u8 output.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_ARG, HIP.
+ */
+int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                         const float* global_scale, int T, int H,
+                         uint8_t* packed, uint8_t* scales, void* stream);
+
+/*
+ * moe_combine — post-expert RMSNorm, weighting and top-k sum.
+ *
+ * Defined by TensorRT-LLM PR #21356, description, Triton kernel "Post-expert
+ * norm and combine" (weight-first RMSNorm of each selected expert row, the
+ * routing weights and the top-k sum per token; a row behind an invalid slot —
+ * negative or past the end of the expert output — is never read) and
+ * "Routing" (the pick order fixes the summation order); TensorRT-LLM PR
+ * #21042, "MoE" (post-expert RMSNorm of each expert output before the
+ * weighted top-k sum).
+ *
+ * For token t, over j = 0..k-1 in order, with r = slots[t,j]:
+ *   skip unless 0 <= r < R (row r of expert_out is then never read)
+ *   z   = bf16( expert_out[r,:] * g / sqrt(mean(expert_out[r,:]^2) + eps) ),
+ *         g = gain_center + norm_w (FP32)
+ *   acc += topk_w[t,j] * z                  (FP32)
+ * out[t,:] = bf16(acc); a token with no valid slot gets +0.0.
+ *
+ *   expert_out [R,H] BF16 bits (R >= 0; may be NULL only if R == 0).
+ *   slots      [T,k] int32 (typically moe_dispatch's dest viewed as [T,k]).
+ *   topk_w     [T,k] FP32.   norm_w [H] FP32.
+ *   gain_center finite, eps >= 0 finite.
+ *   T >= 0, 1 <= k <= MOE_MAX_TOPK, 8 <= H <= MOE_MAX_HIDDEN, H % 8 == 0.
+ *   out [T,H] BF16 bits output.
+ * Errors: NULL_ARG, BAD_SHAPE, BAD_ARG, HIP.
+ */
+int moe_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
+                const float* norm_w, float gain_center, float eps, int T, int H, int k,
+                uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTING_H */

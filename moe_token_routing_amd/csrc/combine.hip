@@ -1,0 +1,184 @@
+// moe_combine: post-expert RMSNorm of each selected expert row, routing-weight
+// scaling and top-k sum, skipping invalid slots.
+//
+// Method: TensorRT-LLM PR #21356 ("Add the Muse Spark Open decoder fast
+// paths"), description, Triton kernel "Post-expert norm and combine" and
+// "Routing" (pick order fixes the summation order); TensorRT-LLM PR #21042
+// ("Add the Muse Spark Open model"), Description, "MoE".
+//
+// Design (gfx950): HBM-bound row gathers. Each token's k expert rows are
+// loaded in groups of G with 16-byte loads spread over the token's threads
+// (so every wave-wide load covers 1 KB of one row), the G sums of squares are
+// reduced together, and the weighted BF16-rounded normalised rows accumulate
+// in FP32 registers in slot order. A slot outside [0, R) issues no load at
+// all. The per-element gain stays in registers across the tokens a block
+// visits (grid-stride loop over tokens).
+#include <cmath>
+
+#include "launch.hpp"
+#include "rows.hpp"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ float round_to_bf16(float f) {
+    return __uint_as_float(f32_to_bf16_rne(f) << 16);
+}
+
+template <int VPT>
+struct CombineCfg {
+    static constexpr int G = (16 / VPT) < 8 ? (16 / VPT) : 8;   // rows loaded per group
+};
+
+template <int VPT>
+__global__ __launch_bounds__(kRowBlock) void combine_kernel(
+    const u32x4* __restrict__ expert_out, int R, const int32_t* __restrict__ slots,
+    const float* __restrict__ topk_w, const float* __restrict__ norm_w, float gain_center,
+    float eps, int T, int H, int k, int tpt, u32x4* __restrict__ out) {
+    constexpr int G = CombineCfg<VPT>::G;
+    __shared__ float red[(kRowBlock / kWave) * G];
+
+    const int nvec = H >> 3;
+    const int tokens_per_block = kRowBlock / tpt;
+    const int sub = threadIdx.x / tpt;
+    const int tid = threadIdx.x - sub * tpt;
+    const float hf = static_cast<float>(H);
+
+    float gain[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int v = tid + i * tpt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gain[i][e] = 0.f;
+        if (v < nvec) {
+            const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
+            const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
+            gain[i][0] = gain_center + a.x; gain[i][1] = gain_center + a.y;
+            gain[i][2] = gain_center + a.z; gain[i][3] = gain_center + a.w;
+            gain[i][4] = gain_center + b.x; gain[i][5] = gain_center + b.y;
+            gain[i][6] = gain_center + b.z; gain[i][7] = gain_center + b.w;
+        }
+    }
+
+    for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
+        const int t = t0 + sub;
+        const bool tok_ok = t < T;
+        float acc[VPT][8];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+
+        for (int j0 = 0; j0 < k; j0 += G) {
+            u32x4 x[G][VPT];
+            float ss[G];
+            bool ok[G];
+            float wt[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int j = j0 + g;
+                int r = -1;
+                wt[g] = 0.f;
+                if (tok_ok && j < k) {
+                    r = slots[static_cast<size_t>(t) * k + j];
+                    wt[g] = topk_w[static_cast<size_t>(t) * k + j];
+                }
+                ok[g] = r >= 0 && r < R;
+                ss[g] = 0.f;
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const int v = tid + i * tpt;
+                    x[g][i] = u32x4{0u, 0u, 0u, 0u};
+                    if (ok[g] && v < nvec)
+                        x[g][i] = load_nt(&expert_out[static_cast<size_t>(r) * nvec + v]);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float a = bf16_lo(w4[q]), b = bf16_hi(w4[q]);
+                        ss[g] += a * a;
+                        ss[g] += b * b;
+                    }
+                }
+            }
+            token_sum(ss, tpt, red);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (!ok[g]) continue;
+                const float rinv = 1.0f / sqrtf(ss[g] / hf + eps);
+                const float w = wt[g];
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float z0 = round_to_bf16(bf16_lo(w4[q]) * gain[i][2 * q] * rinv);
+                        const float z1 = round_to_bf16(bf16_hi(w4[q]) * gain[i][2 * q + 1] * rinv);
+                        acc[i][2 * q] += w * z0;
+                        acc[i][2 * q + 1] += w * z1;
+                    }
+                }
+            }
+        }
+        if (tok_ok) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int v = tid + i * tpt;
+                if (v < nvec) {
+                    u32x4 o;
+                    o.x = pack_bf16x2(acc[i][0], acc[i][1]);
+                    o.y = pack_bf16x2(acc[i][2], acc[i][3]);
+                    o.z = pack_bf16x2(acc[i][4], acc[i][5]);
+                    o.w = pack_bf16x2(acc[i][6], acc[i][7]);
+                    store_nt(o, &out[static_cast<size_t>(t) * nvec + v]);
+                }
+            }
+        }
+    }
+}
+
+template <int VPT>
+int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
+                   const float* norm_w, float gain_center, float eps, int T, int H, int k,
+                   const RowGeom& geo, uint16_t* out, void* stream) {
+    const int tokens_per_block = kRowBlock / geo.tpt;
+    const int needed = ceil_div(T, tokens_per_block);
+    const int cap = device_cu_count() * 8;
+    const int grid = needed < cap ? needed : cap;
+    return launch(combine_kernel<VPT>, dim3(grid), dim3(kRowBlock), 0, stream,
+                  reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
+                  gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_combine(const uint16_t* expert_out, int R, const int32_t* slots,
+                           const float* topk_w, const float* norm_w, float gain_center, float eps,
+                           int T, int H, int k, uint16_t* out, void* stream) {
+    using namespace moe;
+    if (T < 0 || R < 0 || k < 1 || k > MOE_MAX_TOPK || H < 8 || H > MOE_MAX_HIDDEN || H % 8 != 0)
+        return MOE_ERR_BAD_SHAPE;
+    if (static_cast<long long>(T) * k >= (1ll << 31) ||
+        static_cast<long long>(R) * (H / 8) >= (1ll << 40))
+        return MOE_ERR_BAD_SHAPE;
+    if (!std::isfinite(gain_center) || !std::isfinite(eps) || eps < 0.f) return MOE_ERR_BAD_ARG;
+    if (T == 0) return MOE_OK;
+    if (!slots || !topk_w || !norm_w || !out || (R > 0 && !expert_out)) return MOE_ERR_NULL_ARG;
+    if (!all_aligned16(expert_out, slots, topk_w, norm_w, out)) return MOE_ERR_ALIGN;
+    const RowGeom geo = row_geom(H);
+    int vpt = 1;
+    while (vpt < geo.vpt) vpt <<= 1;
+    switch (vpt) {
+        case 1: return launch_combine<1>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
+        case 2: return launch_combine<2>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
+        case 4: return launch_combine<4>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
+        case 8: return launch_combine<8>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
+        default: return MOE_ERR_BAD_SHAPE;
+    }
+}

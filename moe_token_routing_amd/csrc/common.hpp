@@ -1,0 +1,79 @@
+// Shared device helpers of the gfx950 kernels (wave64, CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_routing.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// 16-byte vector of four 32-bit words (a native vector type, so the
+// non-temporal load/store builtins accept it).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_nt(u32x4 v, u32x4* p) { __builtin_nontemporal_store(v, p); }
+
+// ---- BF16 bit patterns ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) {   // element 2m of a packed pair
+    return __uint_as_float(packed << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {   // element 2m+1
+    return __uint_as_float(packed & 0xFFFF0000u);
+}
+
+// FP32 -> BF16, round to nearest even; NaN stays a quiet NaN with its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---- wave reductions (wave64) ---------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+    for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint64_t o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = __lane_id();
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// NULL counts as aligned; NULL checks are separate.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+template <typename... P>
+inline bool all_aligned16(const P*... p) { return (aligned16(p) && ...); }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace moe

@@ -1,0 +1,244 @@
+// moe_dispatch: expert histogram, exclusive prefix scan and stable permutation
+// of the routed slots.
+//
+// Method: lmdeploy PR #4835 ("Intern-S2-Mobius meta-MoE support, MoE gate v2,
+// CP attention fixes"), MoE gate v2 notes: per-tile shared-memory expert
+// histograms, a hierarchical multi-block scan over the tiles for large E, the
+// required validity mask (invalid slots get no entry) and the slot-to-position
+// map cleared to -1.
+//
+// Three launches, all deterministic:
+//   1. hist   one block per tile of slots: LDS histogram of the tile's valid
+//             ids, written as tile_counts[tile][E].
+//   2. scan   blocks over 64-expert columns: for each expert, the exclusive
+//             prefix of its count over the tiles (in place) and its total.
+//   3. place  one block per tile: offsets from the totals (block-wide scan),
+//             per-wave LDS histograms of the tile's four quarters, then each
+//             wave ranks its 64-slot chunks in slot order. Equal ids within a
+//             chunk are matched with ballots over the id bits, so the rank
+//             of a slot is the number of earlier slots with its id: the order
+//             within an expert is ascending slot index.
+#include <cmath>
+
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kDispBlock = 256;
+constexpr int kDispWaves = kDispBlock / kWave;
+constexpr int kMaxTiles = 256;
+
+struct TilePlan {
+    int n;        // slots
+    int tiles;
+    int tile;     // slots per tile, a multiple of kDispBlock
+};
+
+inline TilePlan plan_tiles(long long n) {
+    TilePlan p;
+    p.n = static_cast<int>(n);
+    long long tiles = (n + 1023) / 1024;
+    if (tiles > kMaxTiles) tiles = kMaxTiles;
+    if (tiles < 1) tiles = 1;
+    long long per = (n + tiles - 1) / tiles;
+    per = (per + kDispBlock - 1) / kDispBlock * kDispBlock;
+    if (per < kDispBlock) per = kDispBlock;
+    p.tile = static_cast<int>(per);
+    p.tiles = static_cast<int>((n + per - 1) / per);
+    if (p.tiles < 1) p.tiles = 1;
+    return p;
+}
+
+__device__ __forceinline__ int slot_id(const int32_t* ids, int f, int n, int E) {
+    if (f >= n) return -1;
+    const int v = ids[f];
+    return (v >= 0 && v < E) ? v : -1;
+}
+
+__global__ __launch_bounds__(kDispBlock) void hist_kernel(const int32_t* __restrict__ ids, int n,
+                                                          int E, int tile,
+                                                          int32_t* __restrict__ tile_counts) {
+    extern __shared__ int32_t lds[];
+    for (int e = threadIdx.x; e < E; e += kDispBlock) lds[e] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * tile;
+    for (int i = threadIdx.x; i < tile; i += kDispBlock) {
+        const int id = slot_id(ids, base + i, n, E);
+        if (id >= 0) atomicAdd(&lds[id], 1);
+    }
+    __syncthreads();
+    int32_t* row = tile_counts + static_cast<size_t>(blockIdx.x) * E;
+    for (int e = threadIdx.x; e < E; e += kDispBlock) row[e] = lds[e];
+}
+
+// Block: 64 experts (lane) x 4 segments of tiles (wave).
+__global__ __launch_bounds__(kDispBlock) void scan_kernel(int32_t* __restrict__ tile_counts,
+                                                          int tiles, int E,
+                                                          int32_t* __restrict__ counts) {
+    __shared__ int32_t part[kDispWaves][kWave];
+    const int lane = __lane_id();
+    const int seg = threadIdx.x / kWave;
+    const int e = blockIdx.x * kWave + lane;
+    const int per = (tiles + kDispWaves - 1) / kDispWaves;
+    const int t0 = seg * per;
+    const int t1 = min(tiles, t0 + per);
+    int sum = 0;
+    if (e < E) {
+#pragma unroll 8
+        for (int t = t0; t < t1; ++t) sum += tile_counts[static_cast<size_t>(t) * E + e];
+    }
+    part[seg][lane] = sum;
+    __syncthreads();
+    int run = 0;
+    for (int s = 0; s < seg; ++s) run += part[s][lane];
+    if (e < E) {
+        if (seg == kDispWaves - 1) counts[e] = run + sum;
+        for (int t = t0; t < t1; ++t) {
+            int32_t* p = tile_counts + static_cast<size_t>(t) * E + e;
+            const int c = *p;
+            *p = run;
+            run += c;
+        }
+    }
+}
+
+// LDS layout: off[E + 1] then hist[kDispWaves][E].
+__global__ __launch_bounds__(kDispBlock) void place_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int tile,
+    const int32_t* __restrict__ tile_rel, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ dest) {
+    extern __shared__ int32_t lds[];
+    int32_t* off = lds;
+    int32_t* hist = lds + E + 1;
+    __shared__ int32_t wsum[kDispWaves];
+    const int tid = threadIdx.x;
+    const int lane = __lane_id();
+    const int wave = tid / kWave;
+
+    // (1) offsets = exclusive scan of counts: contiguous chunk per thread.
+    const int chunk = (E + kDispBlock - 1) / kDispBlock;
+    const int c0 = min(E, tid * chunk), c1 = min(E, c0 + chunk);
+    int local = 0;
+    for (int e = c0; e < c1; ++e) local += counts[e];
+    int incl = local;   // inclusive scan over the block, in thread order
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    for (int e = tid; e < kDispWaves * E; e += kDispBlock) hist[e] = 0;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    int run = before + incl - local;
+    for (int e = c0; e < c1; ++e) {
+        off[e] = run;
+        run += counts[e];
+    }
+    if (tid == kDispBlock - 1) off[E] = before + incl;
+    __syncthreads();
+    const int total = off[E];
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += kDispBlock) offsets[e] = off[e];
+
+    // (2) per-wave histograms of the tile's quarters.
+    const int base = blockIdx.x * tile;
+    const int quarter = tile / kDispWaves;          // multiple of 64
+    const int q0 = base + wave * quarter;
+    int32_t* my = hist + wave * E;
+    for (int i = lane; i < quarter; i += kWave) {
+        const int id = slot_id(ids, q0 + i, n, E);
+        if (id >= 0) atomicAdd(&my[id], 1);
+    }
+    __syncthreads();
+    // (3) starting position of each wave's run of each expert.
+    const int32_t* rel = tile_rel + static_cast<size_t>(blockIdx.x) * E;
+    for (int e = tid; e < E; e += kDispBlock) {
+        int p = off[e] + rel[e];
+#pragma unroll
+        for (int w = 0; w < kDispWaves; ++w) {
+            const int c = hist[w * E + e];
+            hist[w * E + e] = p;
+            p += c;
+        }
+    }
+    __syncthreads();
+    // (4) rank and place, 64 slots at a time, in slot order within each wave.
+    const int idbits = 32 - __clz(E);   // ids < E, and E itself marks "no entry"
+    for (int i0 = 0; i0 < quarter; i0 += kWave) {
+        const int f = q0 + i0 + lane;
+        const int id = slot_id(ids, f, n, E);
+        const int key = id >= 0 ? id : E;
+        uint64_t peers = ~0ull;
+        for (int b = 0; b < idbits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t m = ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        if (id >= 0) {
+            const int rank = __popcll(peers & lanemask_lt());
+            const int pos = my[id] + rank;
+            perm[pos] = f;
+            dest[f] = pos;
+            // the last peer lane advances the running position of this id
+            if ((peers >> lane) == 1ull) my[id] = pos + 1;
+        } else if (f < n) {
+            dest[f] = -1;
+        }
+    }
+    // (5) positions past the last valid entry hold -1; each tile clears its own range.
+    for (int p = base + tid; p < base + tile && p < n; p += kDispBlock)
+        if (p >= total) perm[p] = -1;
+}
+
+__global__ __launch_bounds__(kDispBlock) void zero_kernel(int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets, int E) {
+    for (int e = threadIdx.x; e <= E; e += kDispBlock) {
+        if (e < E) counts[e] = 0;
+        offsets[e] = 0;
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_dispatch_workspace_bytes(int T, int k, int E) {
+    using namespace moe;
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    const long long n = static_cast<long long>(T) * k;
+    if (n == 0) return 0;
+    const TilePlan p = plan_tiles(n);
+    const size_t bytes = static_cast<size_t>(p.tiles) * E * sizeof(int32_t);
+    return (bytes + 255) / 256 * 256;
+}
+
+extern "C" int moe_dispatch(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                            int32_t* offsets, int32_t* perm, int32_t* dest, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_BAD_SHAPE;
+    const long long n = static_cast<long long>(T) * k;
+    if (n >= (1ll << 31)) return MOE_ERR_BAD_SHAPE;
+    if (!counts || !offsets) return MOE_ERR_NULL_ARG;
+    if (n > 0 && (!topk_ids || !perm || !dest)) return MOE_ERR_NULL_ARG;
+    if (!all_aligned16(topk_ids, counts, offsets, perm, dest)) return MOE_ERR_ALIGN;
+    if (n == 0)   // no slots: counts and offsets are all zero (a kernel, not a memset node)
+        return launch(zero_kernel, dim3(1), dim3(kDispBlock), 0, stream, counts, offsets, E);
+    const size_t need = moe_dispatch_workspace_bytes(T, k, E);
+    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+    const TilePlan p = plan_tiles(n);
+    int32_t* tile_counts = static_cast<int32_t*>(workspace);
+    int rc = launch(hist_kernel, dim3(p.tiles), dim3(kDispBlock), sizeof(int32_t) * E, stream,
+                    topk_ids, p.n, E, p.tile, tile_counts);
+    if (rc) return rc;
+    rc = launch(scan_kernel, dim3(ceil_div(E, kWave)), dim3(kDispBlock), 0, stream, tile_counts,
+                p.tiles, E, counts);
+    if (rc) return rc;
+    const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) + 1 + static_cast<size_t>(kDispWaves) * E);
+    return launch(place_kernel, dim3(p.tiles), dim3(kDispBlock), lds, stream, topk_ids, p.n, E,
+                  p.tile, static_cast<const int32_t*>(tile_counts),
+                  static_cast<const int32_t*>(counts), offsets, perm, dest);
+}

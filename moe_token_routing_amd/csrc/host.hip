@@ -1,0 +1,36 @@
+// Host-side helpers of the library: status strings and cached device facts.
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace moe {
+
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static int cached[kMaxDevices] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;   // benign race: every thread writes the same value
+    }
+    return cached[dev];
+}
+
+}  // namespace moe
+
+extern "C" const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL_ARG: return "a required pointer is NULL";
+        case MOE_ERR_BAD_SHAPE: return "a size is outside the supported range";
+        case MOE_ERR_BAD_DTYPE: return "unknown dtype code";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_BAD_ARG: return "a scalar argument is out of range";
+        case MOE_ERR_HIP: return "the HIP runtime rejected a launch";
+        case MOE_ERR_ALIGN: return "an array pointer is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,29 @@
+// Host-side launch helper: launches with hipLaunchKernel so the launch status
+// is returned directly (not read from the thread's sticky last-error slot).
+#pragma once
+
+#include <tuple>
+#include <utility>
+
+#include "common.hpp"
+
+namespace moe {
+
+template <typename... KArgs, typename... Args>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, void* stream,
+           Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+    std::tuple<KArgs...> values(std::forward<Args>(args)...);
+    void* ptrs[sizeof...(KArgs)];
+    std::apply([&](auto&... v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, values);
+    return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs,
+                                      shmem, static_cast<hipStream_t>(stream)));
+}
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace moe

@@ -29,7 +29,8 @@ _BF16_MIN_NORMAL_EXP = -126
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Decode BF16 bit patterns (uint16) exactly to float64."""
     u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return u32.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return u32.view(np.float32).astype(np.float64)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,79 @@
+"""Shared helpers of the GPU parity tests: host <-> device transfers and the
+comparison rules of the parity contract."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+DEV = "cuda:0"
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def require_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+def note(msg: str):
+    """Name the case before a GPU step (flushed, so it survives a crash)."""
+    sys.stdout.write("[case] %s\n" % msg)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def scalar_dev(v: float) -> torch.Tensor:
+    return torch.tensor([np.float32(v)], dtype=torch.float32, device=DEV)
+
+
+def assert_bf16_within(got_bits, ref_bits, magnitude, ulps=2.0, what="out"):
+    """|got - ref| <= ulps * ulp_bf16(magnitude), elementwise; NaN must match NaN."""
+    g = O.bf16_bits_to_f64(got_bits)
+    r = O.bf16_bits_to_f64(ref_bits)
+    nan_g, nan_r = np.isnan(g), np.isnan(r)
+    assert np.array_equal(nan_g, nan_r), "%s: NaN pattern differs" % what
+    ok = ~nan_r
+    tol = ulps * O.bf16_ulp(np.maximum(np.abs(magnitude), np.abs(r)))
+    err = np.abs(g - r)
+    bad = ok & (err > tol)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d elements beyond %g BF16 ulp, e.g. %s got %s want %s" % (
+            what, int(bad.sum()), ulps, idx.tolist(), g[bad][:5], r[bad][:5]))
+    return float((g == r)[ok].mean()) if ok.any() else 1.0
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    M = packed.shape[0]
+    c = np.empty((M, packed.shape[1] * 2), dtype=np.uint8)
+    c[:, 0::2] = packed & 0x0F
+    c[:, 1::2] = packed >> 4
+    return c
+
+
+def e2m1_step_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in grid steps between two E2M1 codes (signed values)."""
+    va = np.where(a & 8, -1, 1) * (a & 7).astype(np.int64)
+    vb = np.where(b & 8, -1, 1) * (b & 7).astype(np.int64)
+    # -0 and +0 are one step apart only if a value crossed zero; count index distance
+    return np.abs(va - vb)

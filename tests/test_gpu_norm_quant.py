@@ -1,0 +1,106 @@
+"""moe_norm_quant_nvfp4 against the oracle: codes and scales bit-exact
+outside the stated set of BF16-midpoint blocks, within one step inside it;
+exact everywhere on power-of-two rows; every workload shape."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as wl
+from gpu_helpers import dev, e2m1_step_distance, host, note, require_gpu, scalar_dev, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+m = pytest.importorskip("moe_token_routing_amd")
+
+
+def _run(x, nw, gc, eps, gs, what):
+    require_gpu()
+    note("norm_quant %s T=%d H=%d" % (what, x.shape[0], x.shape[1]))
+    packed, scales = m.norm_quant_nvfp4(dev(x), dev(nw), gc, eps, scalar_dev(gs))
+    torch.cuda.synchronize()
+    return host(packed), host(scales)
+
+
+def _check(x, nw, gc, eps, gs, got_packed, got_scales, rows, what):
+    ref_packed, ref_scales = O.norm_quant_nvfp4(x[rows], nw, gc, eps, gs)
+    near = O.midpoint_boundary_blocks(x[rows], nw, gc, eps)       # [M, H/16]
+    gp, gsf = got_packed[rows], got_scales[rows]
+    gc_, rc_ = unpack_codes(gp), unpack_codes(ref_packed)
+    M, H = gc_.shape
+    nearel = np.repeat(near, 16, axis=1)
+    # outside the stated set: exact
+    assert np.array_equal(gsf[~near], ref_scales[~near]), what + ": scale mismatch outside the stated set"
+    bad = (gc_ != rc_) & ~nearel
+    assert not bad.any(), "%s: %d code mismatches outside the stated set" % (what, int(bad.sum()))
+    # inside: one step at most
+    if near.any():
+        assert (np.abs(gsf[near].astype(int) - ref_scales[near].astype(int)) <= 1).all()
+        assert (e2m1_step_distance(gc_[nearel], rc_[nearel]) <= 1).all()
+    return int(near.sum()), int(((gc_ != rc_) & nearel).sum())
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", 257),
+                                    ("large_e", 100), ("wide_k", 5001)])
+def test_norm_quant_workloads(name, T):
+    w = wl.WORKLOADS[name]
+    T = w.T if T is None else T
+    x = wl.quant_input(w, T)
+    nw = wl.quant_gain(w)
+    y = O.rmsnorm_bf16(x, nw, w.quant_gain_center, w.eps)
+    gs = O.global_scale(y)
+    p, s = _run(x, nw, w.quant_gain_center, w.eps, gs, name)
+    nset, nmis = _check(x, nw, w.quant_gain_center, w.eps, gs, p, s, np.arange(T), name)
+    print("%s: stated-set blocks %d of %d, code mismatches inside %d" % (name, nset, s.size, nmis))
+
+
+def test_norm_quant_prefill_full_size_sampled():
+    w = wl.WORKLOADS["prefill"]
+    x = wl.quant_input(w)
+    nw = wl.quant_gain(w)
+    g = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([g.choice(w.T, 512, replace=False), [0, w.T - 1]]))
+    gs = O.global_scale(O.rmsnorm_bf16(x[rows], nw, w.quant_gain_center, w.eps))
+    p, s = _run(x, nw, w.quant_gain_center, w.eps, gs, "prefill-full")
+    _check(x, nw, w.quant_gain_center, w.eps, gs, p, s, rows, "prefill-full")
+
+
+def test_norm_quant_power_of_two_rows_exact():
+    """Rows of +-2^m with eps = 0 normalise exactly to +-gain; gains sweep the
+    E2M1 thresholds and every E4M3 scale regime (global scale varied)."""
+    g = np.random.default_rng(50)
+    H = 1024
+    T = 48
+    signs = g.choice([-1.0, 1.0], (T, H))
+    x = wl.f32_to_bf16_bits((signs * 2.0 ** g.integers(-6, 6, (T, 1))).astype(np.float32))
+    grid = np.array([0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0, 7.0])
+    gains = np.tile(grid, H // 16) * 2.0 ** np.repeat(g.integers(-8, 8, H // 16), 16)
+    nw = O.round_bf16(gains).astype(np.float32)
+    assert not O.midpoint_boundary_blocks(x, nw, 0.0, 0.0).any()
+    for gs in (1.0, 448.0 * 6 / 7.0 * 2 ** -8, 3.0e-3, 1e5, 0.7):
+        p, s = _run(x, nw, 0.0, 0.0, gs, "pow2 gs=%g" % gs)
+        rp, rs = O.norm_quant_nvfp4(x, nw, 0.0, 0.0, gs)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(p, rp)
+
+
+@pytest.mark.parametrize("H", [16, 48, 272, 2064, 16384])
+def test_norm_quant_widths(H):
+    g = np.random.default_rng(H + 1)
+    T = 29
+    x = wl.f32_to_bf16_bits((g.standard_normal((T, H)) * 3).astype(np.float32))
+    x[3] = 0                                           # an all-zero row
+    x[4, :16] = 0x8000                                 # negative zeros
+    nw = g.uniform(-1, 1, H).astype(np.float32)
+    gs = O.global_scale(O.rmsnorm_bf16(x, nw, 1.0, 1e-6))
+    p, s = _run(x, nw, 1.0, 1e-6, gs, "H=%d" % H)
+    _check(x, nw, 1.0, 1e-6, gs, p, s, np.arange(T), "H=%d" % H)
+    assert (s[3] == 0).all() and (p[3] == 0).all()
+
+
+def test_norm_quant_zero_tokens():
+    require_gpu()
+    p, s = m.norm_quant_nvfp4(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda:0"),
+                              torch.ones(64, dtype=torch.float32, device="cuda:0"), 1.0, 1e-6,
+                              scalar_dev(1.0))
+    assert p.shape == (0, 32) and s.shape == (0, 4)

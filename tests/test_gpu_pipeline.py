@@ -1,0 +1,124 @@
+"""The four calls chained on one stream at the full prefill shape (the
+benchmark's workload and launch configuration), checked end to end against
+the oracle on sampled tokens, and replayed inside a HIP graph."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as wl
+from gpu_helpers import DEV, assert_bf16_within, dev, host, note, require_gpu, scalar_dev
+
+pytestmark = pytest.mark.gpu
+
+m = pytest.importorskip("moe_token_routing_amd")
+
+
+def _inputs(name, T=None):
+    w = wl.WORKLOADS[name]
+    T = w.T if T is None else T
+    d = dict(w=w, T=T, hidden=wl.hidden(w, T), W=wl.router_weight(w), bias=wl.bias(w),
+             mask=wl.token_mask(w, T), x=wl.quant_input(w, T), qw=wl.quant_gain(w),
+             cg=wl.combine_gain(w), eo=wl.expert_out(w, T * w.k))
+    return d
+
+
+def _pipeline(d, gs):
+    w = d["w"]
+    lg, ids, tw = m.route(dev(d["hidden"]), dev(d["W"]), dev(d["bias"]), dev(d["mask"]), w.k)
+    counts, offsets, perm, dest = m.dispatch(ids, w.E)
+    packed, scales = m.norm_quant_nvfp4(dev(d["x"]), dev(d["qw"]), w.quant_gain_center, w.eps, scalar_dev(gs))
+    out = m.combine(dev(d["eo"]), dest.view(d["T"], w.k), tw, dev(d["cg"]), 0.0, w.eps)
+    torch.cuda.synchronize()
+    return dict(lg=host(lg), ids=host(ids), tw=host(tw), counts=host(counts), offsets=host(offsets),
+                perm=host(perm), dest=host(dest), packed=host(packed), scales=host(scales), out=host(out))
+
+
+@pytest.mark.parametrize("name,T", [("prefill", None), ("wide_k", 4096)])
+def test_pipeline_end_to_end(name, T):
+    require_gpu()
+    d = _inputs(name, T)
+    w, T = d["w"], d["T"]
+    g = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([g.choice(T, 256, replace=False), [0, T - 1]]))
+    gs = O.global_scale(O.rmsnorm_bf16(d["x"][rows], d["qw"], w.quant_gain_center, w.eps))
+    note("pipeline %s T=%d" % (name, T))
+    r = _pipeline(d, gs)
+    # route: the oracle's routing of the GPU logits (every token)
+    ids_o, w_o = O.route_from_logits(r["lg"], d["bias"], d["mask"], w.k)
+    np.testing.assert_array_equal(r["ids"], ids_o)
+    assert (np.abs(r["tw"].astype(np.float64) - w_o) <= 1e-5 * np.abs(w_o)).all()
+    # dispatch of those ids (every slot)
+    ref = O.dispatch(r["ids"], w.E)
+    for k_, rv in zip(("counts", "offsets", "perm", "dest"), ref):
+        np.testing.assert_array_equal(r[k_], rv, err_msg=k_)
+    assert r["offsets"][-1] == int(d["mask"].sum()) * w.k
+    # combine through dest (sampled tokens)
+    slots = r["dest"].reshape(T, w.k)
+    ref_out, mag = O.combine(d["eo"], slots[rows], r["tw"][rows], d["cg"], 0.0, w.eps)
+    assert_bf16_within(r["out"][rows], ref_out, mag, 2.0, "pipeline combine")
+    # quant (sampled rows, outside the stated set)
+    rp, rs = O.norm_quant_nvfp4(d["x"][rows], d["qw"], w.quant_gain_center, w.eps, gs)
+    near = O.midpoint_boundary_blocks(d["x"][rows], d["qw"], w.quant_gain_center, w.eps)
+    assert np.array_equal(r["scales"][rows][~near], rs[~near])
+
+
+def test_pipeline_graph_replay():
+    """Capture the four calls in a HIP graph and replay it with new inputs
+    copied into the captured buffers; every replay must equal the eager run."""
+    require_gpu()
+    w = wl.WORKLOADS["decode"]
+    T = w.T
+    d = _inputs("decode")
+    h_d, W_d, b_d, m_d = dev(d["hidden"]), dev(d["W"]), dev(d["bias"]), dev(d["mask"])
+    x_d, qw_d, cg_d, eo_d = dev(d["x"]), dev(d["qw"]), dev(d["cg"]), dev(d["eo"])
+    gs_d = scalar_dev(0.5)
+    lg = torch.empty((T, w.E), dtype=torch.float32, device=DEV)
+    ids = torch.empty((T, w.k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((T, w.k), dtype=torch.float32, device=DEV)
+    ws_r = torch.empty(m.route_workspace_bytes(T, w.H, w.E, w.k, m.MOE_DTYPE_BF16), dtype=torch.uint8, device=DEV)
+    ws_d = torch.empty(max(1, m.dispatch_workspace_bytes(T, w.k, w.E)), dtype=torch.uint8, device=DEV)
+    counts = torch.empty(w.E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(T * w.k, dtype=torch.int32, device=DEV)
+    dest = torch.empty(T * w.k, dtype=torch.int32, device=DEV)
+    packed = torch.empty((T, w.H // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((T, w.H // 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, w.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        m.route(h_d, W_d, b_d, m_d, w.k, logits=lg, topk_ids=ids, topk_w=tw, workspace=ws_r)
+        m.dispatch(ids, w.E, counts=counts, offsets=offsets, perm=perm, dest=dest, workspace=ws_d)
+        m.norm_quant_nvfp4(x_d, qw_d, 1.0, w.eps, gs_d, packed=packed, scales=scales)
+        m.combine(eo_d, dest.view(T, w.k), tw, cg_d, 0.0, w.eps, out=out)
+
+    def snapshot():
+        return [host(t).copy() for t in (lg, ids, tw, counts, offsets, perm, dest, packed, scales, out)]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    g = np.random.default_rng(12)
+    for rep in range(3):
+        note("graph replay %d" % rep)
+        # new inputs in place
+        h_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
+        x_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
+        mk = (g.uniform(size=T) > 0.2).astype(np.uint8)
+        m_d.copy_(dev(mk))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = snapshot()
+        step()
+        torch.cuda.synchronize()
+        eager = snapshot()
+        for a, b in zip(replayed, eager):
+            np.testing.assert_array_equal(a, b)

@@ -230,6 +230,24 @@ def routing_weights(w: Workload, T: Optional[int] = None) -> np.ndarray:
     return u.astype(np.float32)
 
 
+def synthetic_topk_ids(w: Workload, T: Optional[int] = None, mask: Optional[np.ndarray] = None) -> np.ndarray:
+    """Routing ids [T,k] int32 drawn directly (k distinct experts per token,
+    uniformly; hot experts first when the workload has them), -1 for tokens
+    whose mask byte is 0. Stands in for a router's output where a test needs
+    ids without running one."""
+    T = w.T if T is None else T
+    g = rng(w, "slots")
+    g.integers(0, 2)  # separate this use of the stream from combine_slots
+    ids = np.empty((T, w.k), dtype=np.int32)
+    hot = hot_expert_ids(w)
+    pool = hot if len(hot) >= w.k else np.arange(w.E)
+    for t in range(T):
+        ids[t] = g.choice(pool, size=w.k, replace=False)
+    if mask is not None:
+        ids[np.asarray(mask) == 0] = -1
+    return ids
+
+
 def quant_input(w: Workload, T: Optional[int] = None) -> np.ndarray:
     """Pre-expert norm input [T,H] BF16 bits, drawn like the router input
     (hidden_std, outliers) but from its own stream, so it is a distinct buffer."""
