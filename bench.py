@@ -1,0 +1,241 @@
+"""Benchmark of the MoE routing-and-combine hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+One step is one pass of the whole path over one batch of synthetic input:
+moe_route -> moe_dispatch -> moe_norm_quant_nvfp4 -> moe_combine on the
+current stream, inputs resident in HBM, every output and workspace allocated
+before the timed region. The default workload is the 8192-token prefill batch
+(H=8192, E=256, k=8, 5% invalid tokens). Prints one JSON line.
+
+Alongside the throughput the line carries:
+  stages        per-call mean duration (HIP events on the launch stream) and
+                algorithmic bytes / achieved GB/s of each call
+  roofline      the dominant kernel (the combine) against MI355X's 8 TB/s:
+                algorithmic bytes per launch / mean launch duration; `traffic`
+                is the HBM bytes per launch from the committed rocprofv3
+                counter summary, when that was taken on the current kernel
+                source (null otherwise)
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "routed tokens/sec and % of HBM peak, H=8192 E=256 k=8, 8192 tokens"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_prefill_traffic.json")
+COMBINE_SRC = os.path.join(ROOT, "moe_token_routing_amd", "csrc", "combine.hip")
+
+
+def algorithmic_bytes(w, hidden_bytes: int, valid_slots: int):
+    """Bytes each call must move (inputs read once, outputs written once)."""
+    T, H, E, k = w.T, w.H, w.E, w.k
+    return {
+        "route": T * H * hidden_bytes + E * H * 4 + E * 4 + T + T * k * 8,
+        "dispatch": T * k * 4 * 3 + E * 4 + (E + 1) * 4,
+        "norm_quant": T * H * 2 + H * 4 + T * H // 2 + T * H // 16,
+        "combine": T * k * 8 + valid_slots * H * 2 + H * 4 + T * H * 2,
+    }
+
+
+def source_digest(path: str) -> str:
+    h = hashlib.sha256()
+    for p in sorted([path, os.path.join(os.path.dirname(path), "rows.hpp"),
+                     os.path.join(os.path.dirname(path), "common.hpp")]):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per combine launch from the committed counter summary, if it
+    was taken on the current combine source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != source_digest(COMBINE_SRC):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_tokens: int):
+    """The oracle, as it stands, over the first `sample_tokens` tokens of the
+    workload treated as one batch (route -> dispatch -> norm+quant ->
+    combine), with BLAS held to one thread."""
+    import oracle as O
+    import workloads as wl
+    from threadpoolctl import threadpool_limits
+
+    S = sample_tokens
+    hidden = wl.hidden(w, S)
+    W, bias, mask = wl.router_weight(w), wl.bias(w), wl.token_mask(w, S)
+    x, qw, cg = wl.quant_input(w, S), wl.quant_gain(w), wl.combine_gain(w)
+    eo = wl.expert_out(w, S * w.k)
+    gs = np.float32(1.0)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _, _, ids, tw = O.route(hidden, W, bias, mask, w.k)
+        _, _, _, dest = O.dispatch(ids, w.E)
+        O.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs)
+        O.combine(eo, dest.reshape(S, w.k), tw, cg, 0.0, w.eps)
+        dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d tokens of the %s workload as one batch, all four steps, %.1f s" % (S, w.name, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_token_routing_amd as m
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    m.lib()   # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    T, H, E, k = w.T, w.H, w.E, w.k
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    with open(os.path.join(ROOT, "tests", "golden", "global_scales.json")) as f:
+        gs_value = json.load(f)[w.name]["global_scale"]
+
+    mask_np = wl.token_mask(w)
+    hidden = to_dev(wl.hidden(w))
+    W = to_dev(wl.router_weight(w))
+    bias = to_dev(wl.bias(w))
+    mask = to_dev(mask_np)
+    x = to_dev(wl.quant_input(w))
+    qw = to_dev(wl.quant_gain(w))
+    cg = to_dev(wl.combine_gain(w))
+    eo = to_dev(wl.expert_out(w))
+    gs = torch.tensor([gs_value], dtype=torch.float32, device=dev)
+    hdt = m.MOE_DTYPE_F32 if hidden.dtype == torch.float32 else m.MOE_DTYPE_BF16
+
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ws_r = torch.empty(max(1, m.route_workspace_bytes(T, H, E, k, hdt)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, m.dispatch_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    dest = torch.empty(T * k, dtype=torch.int32, device=dev)
+    packed = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, H // 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    slots = dest.view(T, k)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m.route(hidden, W, bias, mask, k, logits=logits, topk_ids=ids, topk_w=tw, workspace=ws_r)
+        if ev is not None:
+            ev[1].record(stream)
+        m.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, dest=dest, workspace=ws_d)
+        if ev is not None:
+            ev[2].record(stream)
+        m.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs, packed=packed, scales=scales)
+        if ev is not None:
+            ev[3].record(stream)
+        m.combine(eo, slots, tw, cg, 0.0, w.eps, out=out)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+
+    names = ["route", "dispatch", "norm_quant", "combine"]
+    stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    valid_slots = int(offsets[-1].item())
+    nbytes = algorithmic_bytes(w, hidden.element_size(), valid_slots)
+    total_bytes = sum(nbytes.values())
+    stages = {n: {"ms": round(stage_ms[n], 4), "bytes": nbytes[n],
+                  "GBps": round(nbytes[n] / (stage_ms[n] * 1e-3) / 1e9, 1)} for n in names}
+    proj_flop = 2.0 * T * H * E
+    stages["route"]["proj_TFLOPs_fp32_equiv"] = round(proj_flop / (stage_ms["route"] * 1e-3) / 1e12, 2)
+
+    comb_gbs = nbytes["combine"] / (stage_ms["combine"] * 1e-3) / 1e9
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    hbm_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    if args.copy_calib:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded numpy PCG64; BF16 storage, FP32 arithmetic, BF16x3 MFMA projection)",
+        "config": {"workload": "%s: T=%d H=%d E=%d k=%d, %d%% invalid tokens" % (
+            w.name, T, H, E, k, round(100 * w.invalid_token_frac)),
+            "tokens": T, "hidden": H, "experts": E, "top_k": k, "valid_tokens": int(mask_np.sum())},
+        "hbm_GBps_algorithmic": round(hbm_gbs, 1),
+        "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "valid_tokens_per_s": round(int(mask_np.sum()) / (ms_per_step * 1e-3), 1),
+        "stages": stages,
+        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic()},
+        "cpu_baseline": None,
+    }
+    if args.cpu_sample > 0:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
