@@ -7,12 +7,15 @@
 // ("Add the Muse Spark Open model"), Description, "MoE".
 //
 // Design (gfx950): HBM-bound row gathers. Each token's k expert rows are
-// loaded in groups of G with 16-byte loads spread over the token's threads
-// (so every wave-wide load covers 1 KB of one row), the G sums of squares are
-// reduced together, and the weighted BF16-rounded normalised rows accumulate
-// in FP32 registers in slot order. A slot outside [0, R) issues no load at
-// all. The per-element gain stays in registers across the tokens a block
-// visits (grid-stride loop over tokens).
+// loaded in groups of G with 16-byte non-temporal loads spread over the
+// token's threads (every wave-wide load covers 1 KB of one row); a slot
+// outside [0, R) issues no load at all. The G sums of squares are reduced
+// together (v_dot2_f32_bf16 on the packed pairs, then across the token's
+// threads), each normalised row is rounded to BF16 two elements at a time
+// (v_cvt_pk_bf16_f32) and the weighted rows accumulate in FP32 registers in
+// slot order (one FMA per element). That is about six VALU operations per
+// element, so the kernel stays under the HBM time. The per-element gain stays
+// in registers across the tokens a block visits (grid-stride loop).
 #include <cmath>
 
 #include "launch.hpp"
@@ -21,13 +24,10 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ float round_to_bf16(float f) {
-    return __uint_as_float(f32_to_bf16_rne(f) << 16);
-}
-
 template <int VPT>
 struct CombineCfg {
-    static constexpr int G = (16 / VPT) < 8 ? (16 / VPT) : 8;   // rows loaded per group
+    // rows per group: 64 data VGPRs per thread for narrow rows, 64 for H=8192
+    static constexpr int G = VPT >= 8 ? 2 : (VPT >= 4 ? 4 : 8);
 };
 
 template <int VPT>
@@ -37,28 +37,25 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     float eps, int T, int H, int k, int tpt, u32x4* __restrict__ out) {
     constexpr int G = CombineCfg<VPT>::G;
     __shared__ float red[(kRowBlock / kWave) * G];
-
+    // gain = gain_center + norm_w, staged once per block. Vector v's eight
+    // values live as gain_lo[v] (elements 0-3) and gain_hi[v] (4-7), so a
+    // wave's 16-byte LDS reads are consecutive.
+    extern __shared__ float4 gain_lds[];
     const int nvec = H >> 3;
+    float4* gain_lo = gain_lds;
+    float4* gain_hi = gain_lds + nvec;
+    for (int v = threadIdx.x; v < nvec; v += kRowBlock) {
+        const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
+        const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
+        gain_lo[v] = make_float4(gain_center + a.x, gain_center + a.y, gain_center + a.z, gain_center + a.w);
+        gain_hi[v] = make_float4(gain_center + b.x, gain_center + b.y, gain_center + b.z, gain_center + b.w);
+    }
+    __syncthreads();
+
     const int tokens_per_block = kRowBlock / tpt;
     const int sub = threadIdx.x / tpt;
     const int tid = threadIdx.x - sub * tpt;
     const float hf = static_cast<float>(H);
-
-    float gain[VPT][8];
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int v = tid + i * tpt;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gain[i][e] = 0.f;
-        if (v < nvec) {
-            const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
-            const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
-            gain[i][0] = gain_center + a.x; gain[i][1] = gain_center + a.y;
-            gain[i][2] = gain_center + a.z; gain[i][3] = gain_center + a.w;
-            gain[i][4] = gain_center + b.x; gain[i][5] = gain_center + b.y;
-            gain[i][6] = gain_center + b.z; gain[i][7] = gain_center + b.w;
-        }
-    }
 
     for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
         const int t = t0 + sub;
@@ -84,27 +81,30 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
                     wt[g] = topk_w[static_cast<size_t>(t) * k + j];
                 }
                 ok[g] = r >= 0 && r < R;
-                ss[g] = 0.f;
+                if (ok[g]) {
+                    const u32x4* row = expert_out + static_cast<size_t>(r) * nvec;
 #pragma unroll
-                for (int i = 0; i < VPT; ++i) {
-                    const int v = tid + i * tpt;
-                    x[g][i] = u32x4{0u, 0u, 0u, 0u};
-                    if (ok[g] && v < nvec)
-                        x[g][i] = load_nt(&expert_out[static_cast<size_t>(r) * nvec + v]);
+                    for (int i = 0; i < VPT; ++i) {
+                        const int v = tid + i * tpt;
+                        if (v < nvec) x[g][i] = load_nt(&row[v]);
+                    }
                 }
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
+                float s = 0.f;
+                if (ok[g]) {
 #pragma unroll
-                for (int i = 0; i < VPT; ++i) {
-                    const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float a = bf16_lo(w4[q]), b = bf16_hi(w4[q]);
-                        ss[g] += a * a;
-                        ss[g] += b * b;
+                    for (int i = 0; i < VPT; ++i) {
+                        if (tid + i * tpt < nvec) {
+                            s = dot2_sq(x[g][i].x, s);
+                            s = dot2_sq(x[g][i].y, s);
+                            s = dot2_sq(x[g][i].z, s);
+                            s = dot2_sq(x[g][i].w, s);
+                        }
                     }
                 }
+                ss[g] = s;
             }
             token_sum(ss, tpt, red);
 #pragma unroll
@@ -114,13 +114,18 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
                 const float w = wt[g];
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
+                    const int v = tid + i * tpt;
+                    if (v >= nvec) continue;
                     const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
+                    const float4 ga = gain_lo[v], gb = gain_hi[v];
+                    const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float z0 = round_to_bf16(bf16_lo(w4[q]) * gain[i][2 * q] * rinv);
-                        const float z1 = round_to_bf16(bf16_hi(w4[q]) * gain[i][2 * q + 1] * rinv);
-                        acc[i][2 * q] += w * z0;
-                        acc[i][2 * q + 1] += w * z1;
+                        const float y0 = (bf16_lo(w4[q]) * gv[2 * q]) * rinv;
+                        const float y1 = (bf16_hi(w4[q]) * gv[2 * q + 1]) * rinv;
+                        const uint32_t z = cvt_pk_bf16(y0, y1);
+                        acc[i][2 * q] = __builtin_fmaf(w, bf16_lo(z), acc[i][2 * q]);
+                        acc[i][2 * q + 1] = __builtin_fmaf(w, bf16_hi(z), acc[i][2 * q + 1]);
                     }
                 }
             }
@@ -131,10 +136,10 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
                 const int v = tid + i * tpt;
                 if (v < nvec) {
                     u32x4 o;
-                    o.x = pack_bf16x2(acc[i][0], acc[i][1]);
-                    o.y = pack_bf16x2(acc[i][2], acc[i][3]);
-                    o.z = pack_bf16x2(acc[i][4], acc[i][5]);
-                    o.w = pack_bf16x2(acc[i][6], acc[i][7]);
+                    o.x = cvt_pk_bf16(acc[i][0], acc[i][1]);
+                    o.y = cvt_pk_bf16(acc[i][2], acc[i][3]);
+                    o.z = cvt_pk_bf16(acc[i][4], acc[i][5]);
+                    o.w = cvt_pk_bf16(acc[i][6], acc[i][7]);
                     store_nt(o, &out[static_cast<size_t>(t) * nvec + v]);
                 }
             }
@@ -148,9 +153,10 @@ int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, cons
                    const RowGeom& geo, uint16_t* out, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
-    const int cap = device_cu_count() * 8;
+    const size_t lds = sizeof(float) * static_cast<size_t>(H);
+    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT>, kRowBlock, lds);
     const int grid = needed < cap ? needed : cap;
-    return launch(combine_kernel<VPT>, dim3(grid), dim3(kRowBlock), 0, stream,
+    return launch(combine_kernel<VPT>, dim3(grid), dim3(kRowBlock), lds, stream,
                   reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
                   gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
 }

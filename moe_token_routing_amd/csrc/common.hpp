@@ -26,6 +26,30 @@ __device__ __forceinline__ float bf16_hi(uint32_t packed) {   // element 2m+1
     return __uint_as_float(packed & 0xFFFF0000u);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// x0^2 + x1^2 + acc for a packed BF16 pair (v_dot2_f32_bf16; the products
+// are exact in FP32).
+__device__ __forceinline__ float dot2_sq(uint32_t packed, float acc) {
+    const bf16x2_t b = __builtin_bit_cast(bf16x2_t, packed);
+    return __builtin_amdgcn_fdot2_f32_bf16(b, b, acc, false);
+}
+
+// Two FP32 values -> packed BF16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+// Lane-wise unsigned maximum of two packed 16-bit pairs (v_pk_max_u16).
+__device__ __forceinline__ uint32_t packed_max_u16(uint32_t a, uint32_t b) {
+    const u16x2_t r = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // FP32 -> BF16, round to nearest even; NaN stays a quiet NaN with its sign.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);

@@ -1,5 +1,7 @@
 // Host-side helpers of the library: status strings and cached device facts.
+#include <functional>
 #include <mutex>
+#include <unordered_map>
 
 #include "launch.hpp"
 
@@ -17,6 +19,37 @@ int device_cu_count() {
         cached[dev] = n;   // benign race: every thread writes the same value
     }
     return cached[dev];
+}
+
+int resident_blocks_impl(const void* kernel, int block, size_t lds) {
+    struct Key {
+        const void* k;
+        int block;
+        size_t lds;
+        int dev;
+        bool operator==(const Key& o) const { return k == o.k && block == o.block && lds == o.lds && dev == o.dev; }
+    };
+    struct Hash {
+        size_t operator()(const Key& x) const {
+            return std::hash<const void*>()(x.k) ^ (std::hash<size_t>()(x.lds) * 31u) ^
+                   (static_cast<size_t>(x.block) << 20) ^ (static_cast<size_t>(x.dev) << 40);
+        }
+    };
+    static std::mutex mu;
+    static std::unordered_map<Key, int, Hash> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const Key key{kernel, block, lds, dev};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds) != hipSuccess || n < 1) n = 1;
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = n;
+    return n;
 }
 
 }  // namespace moe

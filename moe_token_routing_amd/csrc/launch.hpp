@@ -26,4 +26,13 @@ int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, void* 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Blocks of `block` threads with `lds` bytes of dynamic LDS that fit on one
+// CU at once (at least 1); cached per (kernel, block, lds).
+int resident_blocks_impl(const void* kernel, int block, size_t lds);
+
+template <typename... KArgs>
+int resident_blocks(void (*kernel)(KArgs...), int block, size_t lds) {
+    return resident_blocks_impl(reinterpret_cast<const void*>(kernel), block, lds);
+}
+
 }  // namespace moe

@@ -77,6 +77,18 @@ __device__ __forceinline__ uint32_t e2m1_code(float q) {
     return c | (q < 0.f ? 8u : 0u);
 }
 
+// Codes of a packed BF16 pair y times `outs` into byte BYTE of `word`:
+// q = y * outs with -0 turned into +0 (an FMA with a +0 addend rounds once,
+// like the product), then v_cvt_scalef32_pk_fp4_f32 with unit scale, which
+// rounds finite values to the nearest E2M1 value (ties to even code),
+// saturates, and puts the first value in the low nibble.
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t word, uint32_t ypair, float outs) {
+    const float q0 = __builtin_fmaf(bf16_lo(ypair), outs, 0.0f);
+    const float q1 = __builtin_fmaf(bf16_hi(ypair), outs, 0.0f);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, BYTE);
+}
+
 template <int VPT>
 __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
@@ -118,13 +130,13 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
             const int v = tid + i * tpt;
             xv[i] = u32x4{0u, 0u, 0u, 0u};
             if (tok_ok && v < nvec) xv[i] = load_nt(&x[static_cast<size_t>(t) * nvec + v]);
-            const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float a = bf16_lo(w4[q]), b = bf16_hi(w4[q]);
-                ss[0] += a * a;
-                ss[0] += b * b;
-            }
+        for (int i = 0; i < VPT; ++i) {
+            ss[0] = dot2_sq(xv[i].x, ss[0]);
+            ss[0] = dot2_sq(xv[i].y, ss[0]);
+            ss[0] = dot2_sq(xv[i].z, ss[0]);
+            ss[0] = dot2_sq(xv[i].w, ss[0]);
         }
         token_sum(ss, tpt, red);
         const float rinv = 1.0f / sqrtf(ss[0] / hf + eps);
@@ -133,20 +145,20 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
         for (int i = 0; i < VPT; ++i) {
             const int v = tid + i * tpt;
             const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            float y[8];
-            float amax = 0.f;
+            // normalised pairs, rounded once to BF16 (packed)
+            uint32_t yp[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                y[2 * q] = round_to_bf16(bf16_lo(w4[q]) * gain[i][2 * q] * rinv);
-                y[2 * q + 1] = round_to_bf16(bf16_hi(w4[q]) * gain[i][2 * q + 1] * rinv);
-                amax = fmaxf(amax, fmaxf(fabsf(y[2 * q]), fabsf(y[2 * q + 1])));
-            }
-            // NaN-propagating maximum (fmaxf drops NaN): a NaN element makes the block NaN.
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (y[e] != y[e]) amax = y[e];
-            const float other = __shfl_xor(amax, 1, kWave);
-            const float bmax = (other != other) ? other : (amax != amax ? amax : fmaxf(amax, other));
+            for (int q = 0; q < 4; ++q)
+                yp[q] = cvt_pk_bf16((bf16_lo(w4[q]) * gain[i][2 * q]) * rinv,
+                                    (bf16_hi(w4[q]) * gain[i][2 * q + 1]) * rinv);
+            // block maximum of |y|: the magnitude bits of non-negative BF16
+            // values order like integers, and a NaN magnitude exceeds inf.
+            const uint32_t m01 = packed_max_u16(yp[0] & 0x7FFF7FFFu, yp[1] & 0x7FFF7FFFu);
+            const uint32_t m23 = packed_max_u16(yp[2] & 0x7FFF7FFFu, yp[3] & 0x7FFF7FFFu);
+            const uint32_t m = packed_max_u16(m01, m23);
+            uint32_t mbits = max(m & 0xFFFFu, m >> 16);
+            mbits = max(mbits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mbits), 1, kWave)));
+            const float bmax = __uint_as_float(mbits << 16);
             const float tq = bmax * kRcp6;
             const float s = gs * tq;
             const uint32_t sf = e4m3_satfinite(s);
@@ -154,8 +166,21 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
             const float d = sf_f * rcp_gs;
             const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
             uint32_t word = 0;
+            if (mbits < 0x7F80u && fabsf(outs) < INFINITY) {
+                // q = y * out with -0 turned into +0 (fma with a +0 addend, one
+                // rounding); the hardware E2M1 conversion with unit scale rounds
+                // finite values to nearest even and saturates.
+                word = fp4_pair<0>(word, yp[0], outs);
+                word = fp4_pair<1>(word, yp[1], outs);
+                word = fp4_pair<2>(word, yp[2], outs);
+                word = fp4_pair<3>(word, yp[3], outs);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) word |= e2m1_code(y[e] * outs) << (4 * e);
+                for (int q = 0; q < 4; ++q) {
+                    word |= e2m1_code(bf16_lo(yp[q]) * outs) << (8 * q);
+                    word |= e2m1_code(bf16_hi(yp[q]) * outs) << (8 * q + 4);
+                }
+            }
             if (tok_ok && v < nvec) {
                 packed[static_cast<size_t>(t) * nvec + v] = word;
                 if ((v & 1) == 0) scales[static_cast<size_t>(t) * (nvec >> 1) + (v >> 1)] = static_cast<uint8_t>(sf);
