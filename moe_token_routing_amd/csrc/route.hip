@@ -17,17 +17,18 @@
 //    products of the FP32 weights in FP32 (v_mfma_f32_32x32x16_bf16). An FP32
 //    input is split the same way and the six products with plane-index sum
 //    <= 2 are accumulated (the three dropped ones are below 2^-23 of |h*W|).
-//  * Block tile 64 tokens x 64 experts, four waves of 32x32, K staged through
-//    LDS in 32-wide chunks; split-K over a third grid dimension when the
-//    tile grid alone cannot fill the GPU. Partial sums go to the workspace.
-//  * The select kernel (one wave per token) adds the split-K partials in a
-//    fixed order, applies the scale, evaluates the sigmoid in FP64 and rounds
-//    it once, adds the bias in FP32 and picks the top k with k wave-wide
-//    maximum reductions over 64-bit keys (ordered key bits, then inverted
-//    expert id, so an exact tie goes to the lower id).
+//  * Block tile up to 128 tokens x 256 experts (all of them at E = 256, so the
+//    input is read from HBM once), four waves of up to 128 x 64, K staged
+//    through a ring of LDS buffers filled by direct-to-LDS loads several
+//    stages ahead; split-K when the tile grid alone cannot fill the GPU,
+//    arranged so that each XCD reads one K-slice of the weight planes (which
+//    then stays in its L2). Partial sums go to the workspace.
+//  * The selection (select.hip) adds the split-K partials in a fixed order,
+//    applies the scale and picks the top k.
 #include <cmath>
 
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace moe {
 namespace {
@@ -35,266 +36,293 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64;     // tokens per block tile
-constexpr int kBN = 64;     // experts per block tile
-constexpr int kKC = 32;     // K per LDS stage
-constexpr int kLdsRow = kKC + 8;   // padded row (bf16 elements)
-constexpr int kGemmBlock = 256;
-constexpr int kTargetBlocks = 512;
+constexpr int kTargetBlocks = 480;   // about two blocks per CU
 
 // ---------------------------------------------------------------- split ----
 
-// x (FP32) -> three BF16 planes whose sum is x.
+// x (FP32) -> three BF16 values whose sum is x (each the next 8 significant
+// bits of what the previous ones missed).
+__device__ __forceinline__ void split3(float v, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+    p0 = f32_to_bf16_rne(v);
+    const float r1 = v - __uint_as_float(p0 << 16);
+    p1 = f32_to_bf16_rne(r1);
+    const float r2 = r1 - __uint_as_float(p1 << 16);
+    p2 = f32_to_bf16_rne(r2);
+}
+
+// FP32 input rows -> three BF16 planes [3][n] in the input's own layout.
 __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ x, size_t n,
                                                      uint16_t* __restrict__ planes) {
     const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const float v = x[i];
-        const uint32_t p0 = f32_to_bf16_rne(v);
-        const float r1 = v - __uint_as_float(p0 << 16);
-        const uint32_t p1 = f32_to_bf16_rne(r1);
-        const float r2 = r1 - __uint_as_float(p1 << 16);
-        const uint32_t p2 = f32_to_bf16_rne(r2);
+        uint32_t p0, p1, p2;
+        split3(x[i], p0, p1, p2);
         planes[i] = static_cast<uint16_t>(p0);
         planes[n + i] = static_cast<uint16_t>(p1);
         planes[2 * n + i] = static_cast<uint16_t>(p2);
     }
 }
 
+__device__ __forceinline__ int swz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+__device__ __forceinline__ int slot_bytes(int row, int c) { return (row * 2 + (c ^ swz(row))) * 16; }
+
+// Router weight [E,H] FP32 -> its three BF16 planes in the projection's tiled
+// layout: for expert tile j (BN experts) and K-step s (16 columns) one
+// contiguous block of 3*BN rows x 32 bytes, laid out exactly as the LDS stage
+// that receives it (row R = plane*BN + expert-in-tile, chunk c of the row in
+// 16-byte slot 2R + (c ^ swz(R))). A stage's weight tile is then a single
+// contiguous run of memory. Experts beyond E are zero. Block 0 also clears the
+// 256-byte zero block the projection reads in place of out-of-range input.
+// One thread per (tile, expert, K-step, 8-column chunk), K-step fastest so
+// the FP32 reads are contiguous.
+__global__ __launch_bounds__(256) void split_weight_kernel(const float* __restrict__ W, int E, int H,
+                                                           int BN, int tiles_n,
+                                                           u32x4* __restrict__ tiled,
+                                                           uint32_t* __restrict__ zero_block) {
+    if (blockIdx.x == 0 && threadIdx.x < 64) zero_block[threadIdx.x] = 0u;
+    const int nks = H / 16;
+    const long long total = static_cast<long long>(tiles_n) * BN * nks * 2;
+    const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+    for (long long q = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; q < total; q += stride) {
+        const int c = static_cast<int>(q & 1);
+        const int ks = static_cast<int>((q >> 1) % nks);
+        const long long er = (q >> 1) / nks;           // tile * BN + expert-in-tile
+        const int r = static_cast<int>(er % BN);
+        const int tile = static_cast<int>(er / BN);
+        const int e = tile * BN + r;
+        u32x4 o[3] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+        if (e < E) {
+            const float4* src = reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + ks * 16 + c * 8);
+            const float4 a = src[0], b = src[1];
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t p[3][8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) split3(v[j], p[0][j], p[1][j], p[2][j]);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                o[pl] = u32x4{p[pl][0] | (p[pl][1] << 16), p[pl][2] | (p[pl][3] << 16),
+                              p[pl][4] | (p[pl][5] << 16), p[pl][6] | (p[pl][7] << 16)};
+        }
+        const size_t blk = (static_cast<size_t>(tile) * nks + ks) * (3 * BN * 2);   // in 16-byte slots
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) {
+            const int R = pl * BN + r;
+            tiled[blk + 2 * R + (c ^ swz(R))] = o[pl];
+        }
+    }
+}
+
 // ----------------------------------------------------------------- gemm ----
 
-// Loads a [rows x kKC] tile (row stride ld elements) of a BF16 matrix into LDS
-// rows [0, rows_max) with zero fill outside [0, nrows) x [k0, k1).
-__device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ src, int ld, int row0,
-                                           int nrows, int k0, int k1, uint16_t* dst, int tid) {
-    // kBM rows x (kKC / 8) vectors of 16 bytes = 256 vectors: one per thread.
-    const int r = tid >> 2;
-    const int c = (tid & 3) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    const int row = row0 + r;
-    const int k = k0 + c;
-    if (row < nrows && k < k1) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * ld + k);
-    *reinterpret_cast<uint4*>(dst + r * kLdsRow + c) = v;
+// Block tile: BM = 32*MT tokens x BN = 128*NT experts; four waves side by side
+// along the experts, each computing 32*MT x 32*NT with MT x NT accumulators of
+// v_mfma_f32_32x32x16_bf16. K advances in stages of 16 (one MFMA K-step)
+// through a ring of NBUF LDS buffers, filled NBUF-1 stages ahead with
+// direct-to-LDS 16-byte loads (global_load_lds_dwordx4: lane l writes bytes
+// [16 l, 16 l + 16) of the instruction's 1 KB LDS window). Two blocks share a
+// CU, so one block's loads overlap the other's MFMAs.
+//
+// LDS stage layout: rows of 16 BF16 (two 16-byte chunks); the A rows (NA
+// planes x BM) come first, then the B rows (3 planes x BN). Chunk c of row R
+// sits in slot 2 R + (c ^ swz(R)), swz(R) = ((R >> 2) ^ (R >> 3)) & 1, so the
+// 16 (or 8) lanes that read one chunk of 16 (or 8) consecutive rows in one
+// LDS cycle touch distinct banks. The B rows arrive as one contiguous run of
+// the tiled weight planes; the A rows are gathered from the input rows.
+constexpr int kKC = 16;
+constexpr int kGemmBlock = 256;
+constexpr int kGemmWaves = kGemmBlock / kWave;
+
+template <int NA, int MT, int NT>
+struct GemmShape {
+    static constexpr int BM = 32 * MT;
+    static constexpr int BN = 128 * NT;
+    static constexpr int A_ROWS = NA * BM;
+    static constexpr int B_ROWS = 3 * BN;
+    static constexpr int A_LOADS = A_ROWS * 2 / kWave;   // 1 KB load instructions per stage
+    static constexpr int B_LOADS = B_ROWS * 2 / kWave;
+    static constexpr int STAGE = (A_ROWS + B_ROWS) * 32;  // bytes
+    static constexpr int NBUF = 2;
+    static constexpr size_t LDS = static_cast<size_t>(NBUF) * STAGE;
+    // when every wave issues the same number of loads per stage, a wave can
+    // wait for exactly its own loads of the oldest stage
+    static constexpr bool UNIFORM = (A_LOADS % kGemmWaves == 0) && (B_LOADS % kGemmWaves == 0);
+    static constexpr int PER_WAVE = (A_LOADS + B_LOADS) / kGemmWaves;
+};
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations
+// of this wave are outstanding (gfx9 encoding; lgkm and exp counters untouched).
+template <int VM>
+constexpr int vmcnt_imm() {
+    return (VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
-__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* base, int row, int k) {
-    const uint4 v = *reinterpret_cast<const uint4*>(base + row * kLdsRow + k);
-    bf16x8_t f;
-    __builtin_memcpy(&f, &v, 16);
-    return f;
+// One stage of direct-to-LDS loads (K columns [k0, k0 + 16)) into the stage
+// buffer at `base`; input rows beyond T read the zero block; the weight tile
+// of (expert tile n_tile, K-step k0/16) is read as one contiguous block.
+template <typename S>
+__device__ __forceinline__ void issue_stage(char* base, int k0, int kend, int wave, int lane, int m0,
+                                            int n_tile, int T, int H,
+                                            const uint16_t* __restrict__ a_planes, size_t a_plane,
+                                            const uint16_t* __restrict__ w_tiled,
+                                            const uint16_t* __restrict__ zero16) {
+    const int lr = lane >> 1;
+    const int sc = lane & 1;
+    for (int i = wave; i < S::A_LOADS; i += kGemmWaves) {
+        const int R = i * 32 + lr;
+        const int c = sc ^ swz(R);
+        const int p = R / S::BM, r = R - p * S::BM;
+        const int row = m0 + r, k = k0 + c * 8;
+        const uint16_t* src = (row < T && k < kend)
+            ? a_planes + p * a_plane + static_cast<size_t>(row) * H + k : zero16;
+        __builtin_amdgcn_global_load_lds(src, base + i * 1024, 16, 0, 0);
+    }
+    const uint16_t* blk = w_tiled + (static_cast<size_t>(n_tile) * (H / kKC) + k0 / kKC) * (S::B_LOADS * 512);
+    for (int i = wave; i < S::B_LOADS; i += kGemmWaves)
+        __builtin_amdgcn_global_load_lds(blk + i * 512 + lane * 8, base + S::A_ROWS * 32 + i * 1024, 16, 0, 0);
 }
 
-// NA: number of input planes (1 = BF16 input, 3 = split FP32 input).
-template <int NA>
+// Block b works on K-slice b % nsplit and tile b / nsplit. Blocks go to the
+// eight XCDs round-robin, so when nsplit divides 8 every XCD only ever reads
+// one K-slice of the weight planes and keeps it in its own L2.
+template <int NA, int MT, int NT>
 __global__ __launch_bounds__(kGemmBlock) void proj_kernel(
-    const uint16_t* __restrict__ a_planes, const uint16_t* __restrict__ w_planes, int T, int H,
-    int E, int kslice, float* __restrict__ partials) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[NA][kBM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[3][kBN * kLdsRow];
-
+    const uint16_t* __restrict__ a_planes, const uint16_t* __restrict__ w_planes,
+    const uint16_t* __restrict__ zero16, int T, int H, int E, int kslice, int nsplit,
+    int tiles_m, float* __restrict__ partials) {
+    using S = GemmShape<NA, MT, NT>;
+    constexpr int NBUF = S::NBUF;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x;
     const int lane = __lane_id();
     const int wave = tid / kWave;
-    const int wm = (wave >> 1) * 32;   // wave's token offset in the tile
-    const int wn = (wave & 1) * 32;    // wave's expert offset in the tile
-    const int n0 = blockIdx.x * kBN;
-    const int m0 = blockIdx.y * kBM;
-    const int split = blockIdx.z;
+    const int split = blockIdx.x % nsplit;
+    const int tile = blockIdx.x / nsplit;
+    const int m0 = (tile % tiles_m) * S::BM;
+    const int n_tile = tile / tiles_m;
+    const int n0 = n_tile * S::BN;
     const int kbeg = split * kslice;
     const int kend = min(H, kbeg + kslice);
+    const int nstages = (kend - kbeg + kKC - 1) / kKC;
     const size_t a_plane = static_cast<size_t>(T) * H;
-    const size_t w_plane = static_cast<size_t>(E) * H;
 
-    f32x16_t acc;
+    f32x16_t acc[MT][NT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
-    const int frow = lane & 31;          // fragment row (token or expert)
-    const int fk = (lane >> 5) * 8;      // fragment k offset within a 16-wide step
-
-    for (int k0 = kbeg; k0 < kend; k0 += kKC) {
+    const int frow = lane & 31;
+    const int c = lane >> 5;   // chunk: K columns [8c, 8c + 8) of the stage
+    for (int s = 0; s < NBUF - 1 && s < nstages; ++s)
+        issue_stage<S>(lds + s * S::STAGE, kbeg + s * kKC, kend, wave, lane, m0, n_tile, T, H,
+                       a_planes, a_plane, w_planes, zero16);
+    for (int s = 0; s < nstages; ++s) {
+        // wait for this wave's loads of stage s; the later stages may still fly
+        if (S::UNIFORM && NBUF > 2 && s + NBUF - 2 < nstages)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NBUF - 2) * S::PER_WAVE>());
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // every wave's loads of stage s landed; buffer (s-1)%NBUF is free
+        if (s + NBUF - 1 < nstages)
+            issue_stage<S>(lds + ((s + NBUF - 1) % NBUF) * S::STAGE, kbeg + (s + NBUF - 1) * kKC, kend,
+                           wave, lane, m0, n_tile, T, H, a_planes, a_plane, w_planes, zero16);
+        const char* base = lds + (s % NBUF) * S::STAGE;
+        const char* bbase = base + S::A_ROWS * 32;
+        bf16x8_t a[NA][MT], b[3][NT];
 #pragma unroll
-        for (int p = 0; p < NA; ++p) stage_tile(a_planes + p * a_plane, H, m0, T, k0, kend, As[p], tid);
+        for (int p = 0; p < NA; ++p)
 #pragma unroll
-        for (int p = 0; p < 3; ++p) stage_tile(w_planes + p * w_plane, H, n0, E, k0, kend, Bs[p], tid);
-        __syncthreads();
+            for (int mt = 0; mt < MT; ++mt)
+                a[p][mt] = *reinterpret_cast<const bf16x8_t*>(base + slot_bytes(p * S::BM + mt * 32 + frow, c));
 #pragma unroll
-        for (int ks = 0; ks < kKC; ks += 16) {
-            bf16x8_t a[NA], b[3];
+        for (int p = 0; p < 3; ++p)
 #pragma unroll
-            for (int p = 0; p < NA; ++p) a[p] = lds_frag(As[p], wm + frow, ks + fk);
+            for (int nt = 0; nt < NT; ++nt)
+                b[p][nt] = *reinterpret_cast<const bf16x8_t*>(
+                    bbase + slot_bytes(p * S::BN + wave * 32 * NT + nt * 32 + frow, c));
+        // products (input plane, weight plane) in the outer loop, so that
+        // consecutive MFMAs write different accumulators
+        constexpr int NPROD = NA == 1 ? 3 : 6;
+        constexpr int PA[6] = {0, 0, 0, 1, 1, 2};
+        constexpr int PB[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
-            for (int p = 0; p < 3; ++p) b[p] = lds_frag(Bs[p], wn + frow, ks + fk);
-            if constexpr (NA == 1) {
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], acc, 0, 0, 0);
-            } else {
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], acc, 0, 0, 0);
-            }
-        }
-        __syncthreads();
+        for (int q = 0; q < NPROD; ++q)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[q]][mt], b[PB[q]][nt],
+                                                                          acc[mt][nt], 0, 0, 0);
     }
 
     // 32x32 accumulator layout: lane holds column (lane & 31) and rows
     // 8*(i/4) + 4*(lane/32) + (i%4) for i = 0..15.
     float* out = partials + static_cast<size_t>(split) * T * E;
-    const int col = n0 + wn + (lane & 31);
+    const int half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = m0 + wm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (row < T && col < E) out[static_cast<size_t>(row) * E + col] = acc[i];
-    }
-}
-
-// --------------------------------------------------------------- select ----
-
-// Monotone map of FP32 keys to unsigned integers; -0 counts as +0 and NaN
-// ranks below every number.
-__device__ __forceinline__ uint32_t ordered_key(float key) {
-    uint32_t u = __float_as_uint(key);
-    if (u == 0x80000000u) u = 0u;
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float sigmoid_rn(float l) {
-    return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
-}
-
-constexpr int kSelectBlock = 256;   // four tokens per block, one per wave
-
-// EPL: experts per lane (E <= 64 * EPL). Expert e lives in lane e % 64, slot e / 64.
-template <int EPL>
-__global__ __launch_bounds__(kSelectBlock) void select_kernel(
-    const float* __restrict__ partials, int nsplit, float scale, int logits_in,
-    const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
-    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
-    const int lane = __lane_id();
-    const int t = blockIdx.x * (kSelectBlock / kWave) + threadIdx.x / kWave;
-    if (t >= T) return;   // whole wave leaves together
-    const size_t plane = static_cast<size_t>(T) * E;
-
-    float lg[EPL];
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        lg[i] = 0.f;
-        if (e < E) {
-            const size_t idx = static_cast<size_t>(t) * E + e;
-            if (logits_in) {
-                lg[i] = logits[idx];
-            } else {
-                float s = partials[idx];
-                for (int p = 1; p < nsplit; ++p) s += partials[p * plane + idx];
-                lg[i] = s * scale;
-                logits[idx] = lg[i];
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = n0 + wave * 32 * NT + nt * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                if (row < T && col < E) out[static_cast<size_t>(row) * E + col] = acc[mt][nt][i];
             }
         }
-    }
-    const size_t obase = static_cast<size_t>(t) * k;
-    if (token_mask[t] == 0) {
-        for (int j = lane; j < k; j += kWave) {
-            topk_ids[obase + j] = -1;
-            topk_w[obase + j] = 0.f;
-        }
-        return;
-    }
-
-    uint64_t cand[EPL];
-    float sig[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        cand[i] = 0ull;
-        sig[i] = 0.f;
-        if (e < E) {
-            sig[i] = sigmoid_rn(lg[i]);
-            const float key = sig[i] + bias[e];
-            cand[i] = (static_cast<uint64_t>(ordered_key(key)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
-        }
-    }
-
-    int my_id = -1;
-    float my_s = 0.f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0ull;
-        float best_s = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            if (cand[i] > best) {
-                best = cand[i];
-                best_s = sig[i];
-            }
-        }
-        const uint64_t win = wave_max_u64(best);
-        const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
-        const float s_win = __shfl(best_s, id & (kWave - 1), kWave);
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (cand[i] == win) cand[i] = 0ull;
-        if (lane == j) {
-            my_id = id;
-            my_s = s_win;
-        }
-    }
-    // FP32 running sum of the picked sigmoids in pick order (every lane the same).
-    float total = 0.f;
-    for (int j = 0; j < k; ++j) total += __shfl(my_s, j, kWave);
-    if (lane < k) {
-        topk_ids[obase + lane] = my_id;
-        topk_w[obase + lane] = my_s / total;
-    }
 }
 
+// Workspace layout: [zero block 256 B][W planes][input planes (FP32 input)][partials].
 struct RoutePlan {
+    int na, mt, nt;                 // kernel variant
     int tiles_m, tiles_n, nsplit, kslice;
-    size_t w_planes_bytes, a_planes_bytes, partial_bytes;
+    size_t zero_bytes, w_planes_bytes, a_planes_bytes, partial_bytes;
 };
 
 inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Tile shape and split-K count are functions of (T, H, E, dtype) only, so
+// the workspace query and the call always agree.
 inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
     RoutePlan p;
-    p.tiles_m = ceil_div(T, kBM);
-    p.tiles_n = ceil_div(E, kBN);
+    p.na = hidden_dtype == MOE_DTYPE_F32 ? 3 : 1;
+    p.nt = E > 128 ? 2 : 1;
+    p.mt = T >= 2048 ? 4 : (T >= 256 ? 2 : 1);
+    p.tiles_m = ceil_div(T, 32 * p.mt);
+    p.tiles_n = ceil_div(E, 128 * p.nt);
     const int tiles = p.tiles_m * p.tiles_n;
     const int chunks = ceil_div(H, kKC);
-    int ns = ceil_div(kTargetBlocks, tiles > 0 ? tiles : 1);
-    if (ns > chunks) ns = chunks;
-    if (ns < 1) ns = 1;
-    const int per = ceil_div(chunks, ns);   // chunks per split
+    int ns = 1;
+    while (tiles * ns < kTargetBlocks && ns * 2 <= chunks && ns < 64) ns *= 2;
+    const int per = ceil_div(chunks, ns);   // K stages per split
     p.kslice = per * kKC;
     p.nsplit = ceil_div(H, p.kslice);
-    p.w_planes_bytes = round256(static_cast<size_t>(3) * E * H * sizeof(uint16_t));
-    p.a_planes_bytes = hidden_dtype == MOE_DTYPE_F32 ? round256(static_cast<size_t>(3) * T * H * sizeof(uint16_t)) : 0;
+    p.zero_bytes = 256;
+    // tiled planes, padded to whole expert tiles
+    p.w_planes_bytes = round256(static_cast<size_t>(3) * p.tiles_n * 128 * p.nt * H * sizeof(uint16_t));
+    p.a_planes_bytes = p.na == 3 ? round256(static_cast<size_t>(3) * T * H * sizeof(uint16_t)) : 0;
     p.partial_bytes = round256(static_cast<size_t>(p.nsplit) * T * E * sizeof(float));
     return p;
 }
 
-template <int EPL>
-int launch_select(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
-                  const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
-                  void* stream) {
-    const int grid = ceil_div(T, kSelectBlock / kWave);
-    return launch(select_kernel<EPL>, dim3(grid), dim3(kSelectBlock), 0, stream, partials, nsplit,
-                  scale, logits_in, bias, mask, T, E, k, logits, ids, w);
+template <int NA, int MT, int NT>
+int launch_proj(const RoutePlan& p, const uint16_t* a, const uint16_t* w, const uint16_t* zero,
+                int T, int H, int E, float* partials, void* stream) {
+    using S = GemmShape<NA, MT, NT>;
+    static_assert(S::NBUF >= 2, "LDS too small for two stages");
+    return launch(proj_kernel<NA, MT, NT>, dim3(p.tiles_m * p.tiles_n * p.nsplit), dim3(kGemmBlock),
+                  S::LDS, stream, a, w, zero, T, H, E, p.kslice, p.nsplit, p.tiles_m, partials);
 }
 
-int run_select(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
-               const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
-               void* stream) {
-    const int epl = ceil_div(E, kWave);
-#define MOE_SELECT(N) \
-    if (epl <= N) return launch_select<N>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
-    MOE_SELECT(1) MOE_SELECT(2) MOE_SELECT(4) MOE_SELECT(8) MOE_SELECT(16) MOE_SELECT(24)
-    MOE_SELECT(32) MOE_SELECT(40) MOE_SELECT(48) MOE_SELECT(64)
-#undef MOE_SELECT
+int run_proj(const RoutePlan& p, const uint16_t* a, const uint16_t* w, const uint16_t* zero, int T,
+             int H, int E, float* partials, void* stream) {
+#define MOE_PROJ(NA, MT, NT) \
+    if (p.na == NA && p.mt == MT && p.nt == NT) return launch_proj<NA, MT, NT>(p, a, w, zero, T, H, E, partials, stream);
+    MOE_PROJ(1, 1, 1) MOE_PROJ(1, 1, 2) MOE_PROJ(1, 2, 1) MOE_PROJ(1, 2, 2) MOE_PROJ(1, 4, 1) MOE_PROJ(1, 4, 2)
+    MOE_PROJ(3, 1, 1) MOE_PROJ(3, 1, 2) MOE_PROJ(3, 2, 1) MOE_PROJ(3, 2, 2) MOE_PROJ(3, 4, 1) MOE_PROJ(3, 4, 2)
+#undef MOE_PROJ
     return MOE_ERR_BAD_SHAPE;
 }
 
@@ -306,7 +334,7 @@ extern "C" size_t moe_route_workspace_bytes(int T, int H, int E, int k, int hidd
     if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || logits_in) return 0;
     if (hidden_dtype != MOE_DTYPE_F32 && hidden_dtype != MOE_DTYPE_BF16) return 0;
     const RoutePlan p = plan_route(T, H, E, hidden_dtype);
-    return p.w_planes_bytes + p.a_planes_bytes + p.partial_bytes;
+    return p.zero_bytes + p.w_planes_bytes + p.a_planes_bytes + p.partial_bytes;
 }
 
 extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, const float* bias,
@@ -335,29 +363,28 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
     if (!aligned16(workspace)) return MOE_ERR_ALIGN;
     const RoutePlan p = plan_route(T, H, E, hidden_dtype);
     char* ws = static_cast<char*>(workspace);
-    uint16_t* w_planes = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* a_planes = reinterpret_cast<uint16_t*>(ws + p.w_planes_bytes);
-    float* partials = reinterpret_cast<float*>(ws + p.w_planes_bytes + p.a_planes_bytes);
+    uint16_t* zero = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* w_planes = reinterpret_cast<uint16_t*>(ws + p.zero_bytes);
+    uint16_t* a_planes = reinterpret_cast<uint16_t*>(ws + p.zero_bytes + p.w_planes_bytes);
+    float* partials = reinterpret_cast<float*>(ws + p.zero_bytes + p.w_planes_bytes + p.a_planes_bytes);
 
-    const int cus = device_cu_count();
-    const size_t wn = static_cast<size_t>(E) * H;
-    int rc = launch(split3_kernel, dim3(ceil_div(static_cast<long long>(wn), 256 * 4) < cus * 8 ? ceil_div(static_cast<long long>(wn), 256 * 4) : cus * 8),
-                    dim3(256), 0, stream, W, wn, w_planes);
+    const int cap = device_cu_count() * 8;
+    const int bn = 128 * p.nt;
+    const long long wq = static_cast<long long>(p.tiles_n) * bn * (H / kKC) * 2;
+    const int gw = ceil_div(wq, 256);
+    int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, bn,
+                    p.tiles_n, reinterpret_cast<u32x4*>(w_planes), reinterpret_cast<uint32_t*>(zero));
     if (rc) return rc;
-    const dim3 grid(p.tiles_n, p.tiles_m, p.nsplit);
-    if (hidden_dtype == MOE_DTYPE_F32) {
+    const uint16_t* a = static_cast<const uint16_t*>(hidden);
+    if (p.na == 3) {
         const size_t an = static_cast<size_t>(T) * H;
-        rc = launch(split3_kernel, dim3(ceil_div(static_cast<long long>(an), 256 * 4) < cus * 8 ? ceil_div(static_cast<long long>(an), 256 * 4) : cus * 8),
-                    dim3(256), 0, stream, static_cast<const float*>(hidden), an, a_planes);
+        const int ga = ceil_div(static_cast<long long>(an), 256 * 4);
+        rc = launch(split3_kernel, dim3(ga < cap ? ga : cap), dim3(256), 0, stream,
+                    static_cast<const float*>(hidden), an, a_planes);
         if (rc) return rc;
-        rc = launch(proj_kernel<3>, grid, dim3(kGemmBlock), 0, stream,
-                    static_cast<const uint16_t*>(a_planes), static_cast<const uint16_t*>(w_planes),
-                    T, H, E, p.kslice, partials);
-    } else {
-        rc = launch(proj_kernel<1>, grid, dim3(kGemmBlock), 0, stream,
-                    static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_planes),
-                    T, H, E, p.kslice, partials);
+        a = a_planes;
     }
+    rc = run_proj(p, a, w_planes, zero, T, H, E, partials, stream);
     if (rc) return rc;
     return run_select(partials, p.nsplit, scale, 0, bias, token_mask, T, E, k, logits, topk_ids,
                       topk_w, stream);

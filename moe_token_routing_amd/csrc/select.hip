@@ -1,0 +1,231 @@
+// Routing selection of moe_route: sigmoid + bias keys, sorted top-k with
+// lowest-id ties, renormalised weights, per-token validity mask.
+//
+// Method: TensorRT-LLM PR #21356 ("Add the Muse Spark Open decoder fast
+// paths"), description, Triton kernel "Routing" (sigmoid, bias, top-k,
+// renormalised weights; picks sorted by key, an exact tie goes to the lowest
+// expert id); lmdeploy PR #4835, MoE gate v2 (required validity mask: an
+// invalid token produces no routing entry; the aux-loss-free gate uses the
+// bias only to select).
+//
+// Design (gfx950): one wave per token. Expert e lives in lane e % 64. The
+// sigmoid is evaluated in FP64 and rounded once to FP32 (a correctly rounded
+// FP32 sigmoid), the bias added in FP32, and the key mapped to an unsigned
+// integer that orders like the float. Each of the k rounds takes a wave-wide
+// maximum of the lanes' best remaining keys and then, among the lanes holding
+// that key, the minimum expert id (both DPP reductions); the owner retires
+// its entry. The sigmoid of the k winners is recomputed from their logits for
+// the weights, summed in pick order in FP32 and divided once.
+// E <= 512: keys in registers. Larger E: keys and logits staged per wave in LDS.
+#include <cmath>
+
+#include "launch.hpp"
+#include "select.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kSelectBlock = 256;   // four tokens per block, one per wave
+constexpr int kSelectWaves = kSelectBlock / kWave;
+
+// Monotone map of FP32 keys to unsigned integers; -0 counts as +0 and NaN
+// maps to 0, below every number. (A lane with no candidate left is tracked
+// by its own flag, not by a key value.)
+__device__ __forceinline__ uint32_t ordered_key(float key) {
+    uint32_t u = __float_as_uint(key);
+    if (u == 0x80000000u) u = 0u;
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// sigmoid(l) evaluated in FP64 and rounded once to FP32
+__device__ __forceinline__ float sigmoid_rn(float l) {
+    return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
+}
+
+// logit of (t, e): the split partial sums in order, times the scale (and
+// stored), or the caller's logit
+__device__ __forceinline__ float token_logit(const float* __restrict__ partials, int nsplit,
+                                             size_t plane, float scale, int logits_in,
+                                             float* __restrict__ logits, size_t idx) {
+    if (logits_in) return logits[idx];
+    float s = partials[idx];
+#pragma unroll 1
+    for (int p = 1; p < nsplit; ++p) s += partials[p * plane + idx];
+    const float l = s * scale;
+    logits[idx] = l;
+    return l;
+}
+
+// One round's winner given this lane's best remaining candidate (has, bk, be):
+// the largest key, and among equal keys the lowest expert id.
+__device__ __forceinline__ uint32_t round_winner(bool has, uint32_t bk, uint32_t be) {
+    const uint32_t kmax = __reduce_max_sync(~0ull, has ? bk : 0u);
+    return __reduce_min_sync(~0ull, (has && bk == kmax) ? be : 0xFFFFFFFFu);
+}
+
+// The k picks' weights: sigmoid of each winner's logit, FP32 sum in pick
+// order, one division; lane j < k writes pick j.
+__device__ __forceinline__ void write_picks(int lane, int k, int my_id, float my_l,
+                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+    const float my_s = lane < k ? sigmoid_rn(my_l) : 0.f;
+    float total = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) total += __shfl(my_s, j, kWave);
+    if (lane < k) {
+        ids[lane] = my_id;
+        w[lane] = my_s / total;
+    }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
+    const float* __restrict__ partials, int nsplit, float scale, int logits_in,
+    const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
+    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+    const int lane = __lane_id();
+    const int t = blockIdx.x * kSelectWaves + threadIdx.x / kWave;
+    if (t >= T) return;   // whole wave leaves together
+    const size_t plane = static_cast<size_t>(T) * E;
+    const bool valid = token_mask[t] != 0;
+
+    uint32_t key[EPL];
+    float lg[EPL];
+    uint32_t live = 0;   // bit i: slot i (expert lane + 64 i) still a candidate
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        key[i] = 0u;
+        lg[i] = 0.f;
+        if (e < E) {
+            lg[i] = token_logit(partials, nsplit, plane, scale, logits_in, logits,
+                                static_cast<size_t>(t) * E + e);
+            if (valid) {
+                key[i] = ordered_key(sigmoid_rn(lg[i]) + bias[e]);
+                live |= 1u << i;
+            }
+        }
+    }
+    int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
+    float* w = topk_w + static_cast<size_t>(t) * k;
+    if (!valid) {
+        for (int j = lane; j < k; j += kWave) {
+            ids[j] = -1;
+            w[j] = 0.f;
+        }
+        return;
+    }
+
+    int my_id = -1;
+    float my_l = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        uint32_t bk = 0u;
+        int bi = -1;
+        float bl = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const bool take = ((live >> i) & 1u) && (bi < 0 || key[i] > bk);
+            bk = take ? key[i] : bk;
+            bl = take ? lg[i] : bl;
+            bi = take ? i : bi;
+        }
+        const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(lane + kWave * bi));
+        const int owner = static_cast<int>(win & (kWave - 1));
+        const float l_win = __shfl(bl, owner, kWave);
+        if (lane == owner) live &= ~(1u << bi);
+        if (lane == j) {
+            my_id = static_cast<int>(win);
+            my_l = l_win;
+        }
+    }
+    write_picks(lane, k, my_id, my_l, ids, w);
+}
+
+// Any E: each wave stages its token's keys and logits in its own LDS region
+// (dynamic LDS: kSelectWaves * E * 8 bytes). A lane only touches the entries
+// of its own experts, so no barrier is needed.
+__global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
+    const float* __restrict__ partials, int nsplit, float scale, int logits_in,
+    const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
+    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+    extern __shared__ uint32_t sel_lds[];
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kSelectWaves + wave;
+    if (t >= T) return;
+    uint32_t* keys = sel_lds + static_cast<size_t>(wave) * 2 * E;
+    float* lgs = reinterpret_cast<float*>(keys + E);
+    const size_t plane = static_cast<size_t>(T) * E;
+    const bool valid = token_mask[t] != 0;
+#pragma unroll 1
+    for (int e = lane; e < E; e += kWave) {
+        const float l = token_logit(partials, nsplit, plane, scale, logits_in, logits,
+                                    static_cast<size_t>(t) * E + e);
+        lgs[e] = l;
+        keys[e] = valid ? ordered_key(sigmoid_rn(l) + bias[e]) : 0u;
+    }
+    int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
+    float* w = topk_w + static_cast<size_t>(t) * k;
+    if (!valid) {
+        for (int j = lane; j < k; j += kWave) {
+            ids[j] = -1;
+            w[j] = 0.f;
+        }
+        return;
+    }
+    const int nloc = lane < E ? (E - lane + kWave - 1) / kWave : 0;   // <= 64
+    uint64_t live = nloc >= 64 ? ~0ull : ((1ull << nloc) - 1);
+
+    int my_id = -1;
+    float my_l = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        uint32_t bk = 0u;
+        int bi = -1;
+#pragma unroll 1
+        for (int i = 0; i < nloc; ++i) {
+            if (!((live >> i) & 1ull)) continue;
+            const uint32_t kv = keys[lane + kWave * i];
+            if (bi < 0 || kv > bk) {
+                bk = kv;
+                bi = i;
+            }
+        }
+        const float bl = bi >= 0 ? lgs[lane + kWave * bi] : 0.f;
+        const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(lane + kWave * bi));
+        const int owner = static_cast<int>(win & (kWave - 1));
+        const float l_win = __shfl(bl, owner, kWave);
+        if (lane == owner) live &= ~(1ull << bi);
+        if (lane == j) {
+            my_id = static_cast<int>(win);
+            my_l = l_win;
+        }
+    }
+    write_picks(lane, k, my_id, my_l, ids, w);
+}
+
+template <int EPL>
+int launch_select_reg(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
+                      const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
+                      void* stream) {
+    return launch(select_reg_kernel<EPL>, dim3(ceil_div(T, kSelectWaves)), dim3(kSelectBlock), 0,
+                  stream, partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w);
+}
+
+}  // namespace
+
+int run_select(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
+               const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
+               void* stream) {
+    const int epl = ceil_div(E, kWave);
+    if (epl <= 1) return launch_select_reg<1>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
+    if (epl <= 2) return launch_select_reg<2>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
+    if (epl <= 4) return launch_select_reg<4>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
+    if (epl <= 8) return launch_select_reg<8>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
+    const size_t lds = static_cast<size_t>(kSelectWaves) * 2 * E * sizeof(uint32_t);
+    return launch(select_lds_kernel, dim3(ceil_div(T, kSelectWaves)), dim3(kSelectBlock), lds, stream,
+                  partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w);
+}
+
+}  // namespace moe

@@ -1,0 +1,16 @@
+// Routing selection (sigmoid + bias keys, sorted top-k, renormalised weights,
+// validity mask), shared by moe_route's projection and logits-in modes.
+#pragma once
+
+#include <stdint.h>
+
+namespace moe {
+
+// Per token t: logits[t,e] = scale * sum_p partials[p][t][e] (written to
+// `logits`), or read from `logits` when logits_in != 0 (partials unused);
+// then ids/weights as moe_route defines them. Returns a moe_status.
+int run_select(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
+               const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
+               void* stream);
+
+}  // namespace moe
