@@ -104,7 +104,9 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run one 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
+                    help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
+    ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
+                    help="skip the 1 GiB device-copy reference bandwidth")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
@@ -201,11 +203,23 @@ def main():
     tokens_per_s = T / (ms_per_step * 1e-3)
     hbm_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
 
-    if args.copy_calib:
-        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
-        b = torch.empty_like(a)
-        torch.neg(a, out=b)
+    # Reference point for the HBM-bound kernels: a plain 1 GiB elementwise
+    # copy (torch.neg on int16: 1 GiB read + 1 GiB written), timed on its own.
+    copy_gbs = None
+    if args.copy_calib or args.copy_ref:
+        ca = torch.zeros(1 << 29, dtype=torch.int16, device=dev)
+        cb = torch.empty_like(ca)
+        torch.neg(ca, out=cb)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        reps = 5
+        for _ in range(reps):
+            torch.neg(ca, out=cb)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2.0 * (1 << 30) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del ca, cb
 
     result = {
         "metric": METRIC,
@@ -227,6 +241,8 @@ def main():
         "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "valid_tokens_per_s": round(int(mask_np.sum()) / (ms_per_step * 1e-3), 1),
         "stages": stages,
+        "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
+        "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic()},

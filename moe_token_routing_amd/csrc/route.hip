@@ -73,42 +73,40 @@ __device__ __forceinline__ int slot_bytes(int row, int c) { return (row * 2 + (c
 // 16-byte slot 2R + (c ^ swz(R))). A stage's weight tile is then a single
 // contiguous run of memory. Experts beyond E are zero. Block 0 also clears the
 // 256-byte zero block the projection reads in place of out-of-range input.
-// One thread per (tile, expert, K-step, 8-column chunk), K-step fastest so
-// the FP32 reads are contiguous.
+//
+// One thread per 16-byte output slot, in memory order (the writes stream);
+// each reads the 8 FP32 weights its slot holds a plane of.
 __global__ __launch_bounds__(256) void split_weight_kernel(const float* __restrict__ W, int E, int H,
                                                            int BN, int tiles_n,
                                                            u32x4* __restrict__ tiled,
                                                            uint32_t* __restrict__ zero_block) {
     if (blockIdx.x == 0 && threadIdx.x < 64) zero_block[threadIdx.x] = 0u;
     const int nks = H / 16;
-    const long long total = static_cast<long long>(tiles_n) * BN * nks * 2;
+    const int slots_per_block = 3 * BN * 2;
+    const long long total = static_cast<long long>(tiles_n) * nks * slots_per_block;
     const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
-    for (long long q = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; q < total; q += stride) {
-        const int c = static_cast<int>(q & 1);
-        const int ks = static_cast<int>((q >> 1) % nks);
-        const long long er = (q >> 1) / nks;           // tile * BN + expert-in-tile
-        const int r = static_cast<int>(er % BN);
-        const int tile = static_cast<int>(er / BN);
+    for (long long s = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; s < total; s += stride) {
+        const long long blk = s / slots_per_block;        // tile * nks + K-step
+        const int sl = static_cast<int>(s - blk * slots_per_block);
+        const int tile = static_cast<int>(blk / nks);
+        const int ks = static_cast<int>(blk - static_cast<long long>(tile) * nks);
+        const int R = sl >> 1;
+        const int c = (sl & 1) ^ swz(R);
+        const int pl = R / BN, r = R - pl * BN;
         const int e = tile * BN + r;
-        u32x4 o[3] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+        uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         if (e < E) {
             const float4* src = reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + ks * 16 + c * 8);
             const float4 a = src[0], b = src[1];
             const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-            uint32_t p[3][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) split3(v[j], p[0][j], p[1][j], p[2][j]);
-#pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
-                o[pl] = u32x4{p[pl][0] | (p[pl][1] << 16), p[pl][2] | (p[pl][3] << 16),
-                              p[pl][4] | (p[pl][5] << 16), p[pl][6] | (p[pl][7] << 16)};
+            for (int j = 0; j < 8; ++j) {
+                uint32_t p0, p1, p2;
+                split3(v[j], p0, p1, p2);
+                h[j] = pl == 0 ? p0 : (pl == 1 ? p1 : p2);
+            }
         }
-        const size_t blk = (static_cast<size_t>(tile) * nks + ks) * (3 * BN * 2);   // in 16-byte slots
-#pragma unroll
-        for (int pl = 0; pl < 3; ++pl) {
-            const int R = pl * BN + r;
-            tiled[blk + 2 * R + (c ^ swz(R))] = o[pl];
-        }
+        tiled[s] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
 }
 
@@ -370,8 +368,8 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
 
     const int cap = device_cu_count() * 8;
     const int bn = 128 * p.nt;
-    const long long wq = static_cast<long long>(p.tiles_n) * bn * (H / kKC) * 2;
-    const int gw = ceil_div(wq, 256);
+    const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * 6 * bn;
+    const int gw = ceil_div(wslots, 256);
     int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, bn,
                     p.tiles_n, reinterpret_cast<u32x4*>(w_planes), reinterpret_cast<uint32_t*>(zero));
     if (rc) return rc;

@@ -8,7 +8,9 @@
 // invalid token produces no routing entry; the aux-loss-free gate uses the
 // bias only to select).
 //
-// Design (gfx950): one wave per token. Expert e lives in lane e % 64. The
+// Design (gfx950): one wave per token. For E <= 512 the experts of a lane are
+// consecutive (lane e / EPL), so logits and split partials arrive as 16-byte
+// vector loads; beyond that expert e lives in lane e % 64 of an LDS copy. The
 // sigmoid is evaluated in FP64 and rounded once to FP32 (a correctly rounded
 // FP32 sigmoid), the bias added in FP32, and the key mapped to an unsigned
 // integer that orders like the float. Each of the k rounds takes a wave-wide
@@ -78,6 +80,26 @@ __device__ __forceinline__ void write_picks(int lane, int k, int my_id, float my
     }
 }
 
+// EPL consecutive floats at p (16-byte vector loads when `vec`, which the
+// caller sets when the row length keeps them aligned).
+template <int EPL>
+__device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, int n, float (&v)[EPL]) {
+    if constexpr (EPL % 4 == 0) {
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < EPL; i += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(p + i);
+                v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = i < n ? p[i] : 0.f;
+}
+
+// Experts e = EPL*lane + i (i < EPL) live in lane e / EPL, so each lane reads
+// its logits (or split partials) as one contiguous run.
 template <int EPL>
 __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
@@ -88,22 +110,39 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     if (t >= T) return;   // whole wave leaves together
     const size_t plane = static_cast<size_t>(T) * E;
     const bool valid = token_mask[t] != 0;
+    const int e0 = EPL * lane;
+    const int n = E - e0 < EPL ? (E - e0 > 0 ? E - e0 : 0) : EPL;   // experts of this lane
+    const bool vec = (E % 4) == 0 && n == EPL;
+    const size_t row = static_cast<size_t>(t) * E + e0;
 
-    uint32_t key[EPL];
     float lg[EPL];
-    uint32_t live = 0;   // bit i: slot i (expert lane + 64 i) still a candidate
+    if (n > 0) {
+        if (logits_in) {
+            load_run<EPL>(logits + row, vec, n, lg);
+        } else {
+            load_run<EPL>(partials + row, vec, n, lg);
+#pragma unroll 1
+            for (int p = 1; p < nsplit; ++p) {
+                float q[EPL];
+                load_run<EPL>(partials + p * plane + row, vec, n, q);
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) lg[i] += q[i];
+            }
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                lg[i] *= scale;
+                if (i < n) logits[row + i] = lg[i];
+            }
+        }
+    }
+    uint32_t key[EPL];
+    uint32_t live = 0;   // bit i: expert EPL*lane + i still a candidate
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
         key[i] = 0u;
-        lg[i] = 0.f;
-        if (e < E) {
-            lg[i] = token_logit(partials, nsplit, plane, scale, logits_in, logits,
-                                static_cast<size_t>(t) * E + e);
-            if (valid) {
-                key[i] = ordered_key(sigmoid_rn(lg[i]) + bias[e]);
-                live |= 1u << i;
-            }
+        if (valid && i < n) {
+            key[i] = ordered_key(sigmoid_rn(lg[i]) + bias[e0 + i]);
+            live |= 1u << i;
         }
     }
     int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
@@ -130,8 +169,8 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
             bl = take ? lg[i] : bl;
             bi = take ? i : bi;
         }
-        const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(lane + kWave * bi));
-        const int owner = static_cast<int>(win & (kWave - 1));
+        const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(e0 + bi));
+        const int owner = static_cast<int>(win / EPL);
         const float l_win = __shfl(bl, owner, kWave);
         if (lane == owner) live &= ~(1u << bi);
         if (lane == j) {
