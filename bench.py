@@ -1,16 +1,27 @@
 """Benchmark of the MoE routing-and-combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+                    [--schedule overlap|serial] [--no-graph]
 
 One step is one pass of the whole path over one batch of synthetic input:
-moe_route -> moe_dispatch -> moe_norm_quant_nvfp4 -> moe_combine on the
-current stream, inputs resident in HBM, every output and workspace allocated
-before the timed region. The default workload is the 8192-token prefill batch
-(H=8192, E=256, k=8, 5% invalid tokens). Prints one JSON line.
+moe_route -> moe_dispatch -> moe_combine, and moe_norm_quant_nvfp4, with
+inputs resident in HBM and every output and workspace allocated before the
+timed region. The default workload is the 8192-token prefill batch (H=8192,
+E=256, k=8, 5% invalid tokens). Prints one JSON line.
+
+Schedules (the headline is the default, overlap + graph):
+  serial   the four calls in order on one stream
+  overlap  norm + quant on a second stream beside route -> dispatch ->
+           combine (it depends on none of them); the step forks from the
+           main stream and joins back into it, so it ends when both are done
+  graph    the step captured once in a HIP graph and replayed per step (no
+           per-launch host overhead); every kernel still runs every step
 
 Alongside the throughput the line carries:
-  stages        per-call mean duration (HIP events on the launch stream) and
-                algorithmic bytes / achieved GB/s of each call
+  stages        per-call mean duration (HIP events on the launch stream, from
+                a serial eager pass) and algorithmic bytes / achieved GB/s
+  schedules     ms per step of every schedule, and of the serial one with the
+                256 MB last-level cache flushed before each step (cold)
   roofline      the dominant kernel (the combine) against MI355X's 8 TB/s:
                 algorithmic bytes per launch / mean launch duration; `traffic`
                 is the HBM bytes per launch from the committed rocprofv3
@@ -107,6 +118,12 @@ def main():
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
                     help="skip the 1 GiB device-copy reference bandwidth")
+    ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
+                    help="headline schedule: norm+quant beside the route on a second stream, or all on one")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch the headline schedule eagerly instead of replaying a HIP graph")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="serial steps timed after flushing the last-level cache (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
@@ -160,33 +177,95 @@ def main():
     slots = dest.view(T, k)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def route_():
         m.route(hidden, W, bias, mask, k, logits=logits, topk_ids=ids, topk_w=tw, workspace=ws_r)
-        if ev is not None:
-            ev[1].record(stream)
-        m.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, dest=dest, workspace=ws_d)
-        if ev is not None:
-            ev[2].record(stream)
-        m.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs, packed=packed, scales=scales)
-        if ev is not None:
-            ev[3].record(stream)
-        m.combine(eo, slots, tw, cg, 0.0, w.eps, out=out)
-        if ev is not None:
-            ev[4].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    def dispatch_():
+        m.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, dest=dest, workspace=ws_d)
+
+    def norm_quant_():
+        m.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs, packed=packed, scales=scales)
+
+    def combine_():
+        m.combine(eo, slots, tw, cg, 0.0, w.eps, out=out)
+
+    def step_serial(ev=None):
+        main = torch.cuda.current_stream(dev)
+        for j, call in enumerate((route_, dispatch_, norm_quant_, combine_)):
+            if ev is not None:
+                ev[j].record(main)
+            call()
+        if ev is not None:
+            ev[4].record(main)
+
+    aux = torch.cuda.Stream(device=dev)   # default priority
+
+    def step_overlap():
+        main = torch.cuda.current_stream(dev)
+        aux.wait_stream(main)              # fork
+        with torch.cuda.stream(aux):
+            norm_quant_()
+        route_()
+        dispatch_()
+        combine_()
+        main.wait_stream(aux)              # join: the step ends when both are done
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / steps
+
+    head_step = step_overlap if args.schedule == "overlap" else step_serial
+    # warm up eagerly on a side stream (as graph capture requires), then capture
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(max(1, args.warmup)):
+            head_step()
+    stream.wait_stream(side)
     torch.cuda.synchronize()
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            head_step()
+        torch.cuda.synchronize()
+        head_fn = graph.replay
+        for _ in range(args.warmup):
+            head_fn()
+    else:
+        head_fn = head_step
+
+    # headline: exactly K steps between two synchronizations
+    ms_per_step = timed(head_fn, args.steps)
+    head_name = ("two-stream overlap" if args.schedule == "overlap" else "serial") + \
+        (", HIP graph replay" if args.graph else ", eager launches")
+
+    # serial eager pass with per-call events on the launch stream
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step_serial(events[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    serial_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    overlap_eager_ms = timed(step_overlap, args.steps)
+
+    # cold: flush the 256 MB last-level cache (a 512 MiB write) before each step
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.cold_steps)]
+        for a, b in ce:
+            flush.fill_(1)
+            a.record(stream)
+            step_serial()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = float(np.mean([a.elapsed_time(b) for a, b in ce]))
+        del flush
 
     names = ["route", "dispatch", "norm_quant", "combine"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
@@ -241,6 +320,9 @@ def main():
         "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "valid_tokens_per_s": round(int(mask_np.sum()) / (ms_per_step * 1e-3), 1),
         "stages": stages,
+        "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
+                      "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
+                      "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4)},
         "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),

@@ -18,11 +18,13 @@
 //    input is split the same way and the six products with plane-index sum
 //    <= 2 are accumulated (the three dropped ones are below 2^-23 of |h*W|).
 //  * Block tile up to 128 tokens x 256 experts (all of them at E = 256, so the
-//    input is read from HBM once), four waves of up to 128 x 64, K staged
-//    through a ring of LDS buffers filled by direct-to-LDS loads several
-//    stages ahead; split-K when the tile grid alone cannot fill the GPU,
-//    arranged so that each XCD reads one K-slice of the weight planes (which
-//    then stays in its L2). Partial sums go to the workspace.
+//    input is read from HBM once), four waves of up to 128 x 64. The input
+//    rows, shared by the four waves, go through a ring of LDS stages filled
+//    by direct-to-LDS loads; the weight planes are stored pre-split in MFMA
+//    fragment order and each wave loads its own fragments straight into
+//    registers. Split-K when the tile grid alone cannot fill the GPU, arranged
+//    so that each XCD reads one K-slice of the weight planes (which then
+//    stays in its L2). Partial sums go to the workspace.
 //  * The selection (select.hip) adds the split-K partials in a fixed order,
 //    applies the scale and picks the top k.
 #include <cmath>
@@ -66,37 +68,38 @@ __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ x
 __device__ __forceinline__ int swz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 __device__ __forceinline__ int slot_bytes(int row, int c) { return (row * 2 + (c ^ swz(row))) * 16; }
 
-// Router weight [E,H] FP32 -> its three BF16 planes in the projection's tiled
-// layout: for expert tile j (BN experts) and K-step s (16 columns) one
-// contiguous block of 3*BN rows x 32 bytes, laid out exactly as the LDS stage
-// that receives it (row R = plane*BN + expert-in-tile, chunk c of the row in
-// 16-byte slot 2R + (c ^ swz(R))). A stage's weight tile is then a single
-// contiguous run of memory. Experts beyond E are zero. Block 0 also clears the
-// 256-byte zero block the projection reads in place of out-of-range input.
+// Router weight [E,H] FP32 -> its three BF16 planes as MFMA B fragments.
+// For expert tile j (BN = 32 G experts) and K-step s (16 columns), one
+// contiguous run of 3 G fragments of 1 KB, fragment (plane p, group g) at
+// index p G + g; lane l of a fragment holds 8 consecutive K values
+// [16 s + 8 (l >> 5), +8) of expert 32 (G j + g) + (l & 31) -- exactly the
+// B operand of v_mfma_f32_32x32x16_bf16 for those 32 experts, so one wave
+// loads a fragment with one 16-byte load per lane. Experts beyond E are zero.
+// Block 0 also clears the 256-byte zero block the projection reads in place
+// of out-of-range input.
 //
 // One thread per 16-byte output slot, in memory order (the writes stream);
 // each reads the 8 FP32 weights its slot holds a plane of.
 __global__ __launch_bounds__(256) void split_weight_kernel(const float* __restrict__ W, int E, int H,
-                                                           int BN, int tiles_n,
-                                                           u32x4* __restrict__ tiled,
+                                                           int G, int tiles_n,
+                                                           u32x4* __restrict__ frags,
                                                            uint32_t* __restrict__ zero_block) {
     if (blockIdx.x == 0 && threadIdx.x < 64) zero_block[threadIdx.x] = 0u;
     const int nks = H / 16;
-    const int slots_per_block = 3 * BN * 2;
-    const long long total = static_cast<long long>(tiles_n) * nks * slots_per_block;
+    const int slots_per_step = 3 * G * 64;
+    const long long total = static_cast<long long>(tiles_n) * nks * slots_per_step;
     const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
     for (long long s = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; s < total; s += stride) {
-        const long long blk = s / slots_per_block;        // tile * nks + K-step
-        const int sl = static_cast<int>(s - blk * slots_per_block);
+        const long long blk = s / slots_per_step;         // tile * nks + K-step
+        const int sl = static_cast<int>(s - blk * slots_per_step);
         const int tile = static_cast<int>(blk / nks);
         const int ks = static_cast<int>(blk - static_cast<long long>(tile) * nks);
-        const int R = sl >> 1;
-        const int c = (sl & 1) ^ swz(R);
-        const int pl = R / BN, r = R - pl * BN;
-        const int e = tile * BN + r;
+        const int frag = sl >> 6, l = sl & 63;
+        const int pl = frag / G, g = frag - pl * G;
+        const int e = (tile * G + g) * 32 + (l & 31);
         uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         if (e < E) {
-            const float4* src = reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + ks * 16 + c * 8);
+            const float4* src = reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + ks * 16 + (l >> 5) * 8);
             const float4 a = src[0], b = src[1];
             const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -106,89 +109,72 @@ __global__ __launch_bounds__(256) void split_weight_kernel(const float* __restri
                 h[j] = pl == 0 ? p0 : (pl == 1 ? p1 : p2);
             }
         }
-        tiled[s] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        frags[s] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
 }
 
 // ----------------------------------------------------------------- gemm ----
 
-// Block tile: BM = 32*MT tokens x BN = 128*NT experts; four waves side by side
-// along the experts, each computing 32*MT x 32*NT with MT x NT accumulators of
-// v_mfma_f32_32x32x16_bf16. K advances in stages of 16 (one MFMA K-step)
-// through a ring of NBUF LDS buffers, filled NBUF-1 stages ahead with
-// direct-to-LDS 16-byte loads (global_load_lds_dwordx4: lane l writes bytes
-// [16 l, 16 l + 16) of the instruction's 1 KB LDS window). Two blocks share a
-// CU, so one block's loads overlap the other's MFMAs.
+// Block tile: BM = 32*MT tokens x BN = 128*NT experts; four waves side by
+// side along the experts, each computing 32*MT x 32*NT with MT x NT
+// accumulators of v_mfma_f32_32x32x16_bf16. K advances in steps of 16 (one
+// MFMA K-step).
 //
-// LDS stage layout: rows of 16 BF16 (two 16-byte chunks); the A rows (NA
-// planes x BM) come first, then the B rows (3 planes x BN). Chunk c of row R
-// sits in slot 2 R + (c ^ swz(R)), swz(R) = ((R >> 2) ^ (R >> 3)) & 1, so the
-// 16 (or 8) lanes that read one chunk of 16 (or 8) consecutive rows in one
-// LDS cycle touch distinct banks. The B rows arrive as one contiguous run of
-// the tiled weight planes; the A rows are gathered from the input rows.
+// The waves of a block share the input rows but not the weights, so only the
+// input goes through LDS: a ring of DA stages filled DA-1 steps ahead by
+// direct-to-LDS 16-byte loads (global_load_lds_dwordx4: lane l writes bytes
+// [16 l, 16 l + 16) of the instruction's 1 KB LDS window). Each wave loads its
+// own weight fragments straight into registers one step ahead (two register
+// sets), which keeps the weight traffic out of LDS. Two blocks share a CU, so
+// one block's waits overlap the other's MFMAs.
+//
+// LDS stage layout: rows of 16 BF16 (two 16-byte chunks), NA planes x BM
+// rows. Chunk c of row R sits in slot 2 R + (c ^ swz(R)),
+// swz(R) = ((R >> 2) ^ (R >> 3)) & 1, so the 16 (or 8) lanes that read one
+// chunk of 16 (or 8) consecutive rows in one LDS cycle touch distinct banks.
 constexpr int kKC = 16;
 constexpr int kGemmBlock = 256;
 constexpr int kGemmWaves = kGemmBlock / kWave;
+constexpr int kARing = 8;   // input stages in flight
 
 template <int NA, int MT, int NT>
 struct GemmShape {
     static constexpr int BM = 32 * MT;
     static constexpr int BN = 128 * NT;
+    static constexpr int G = BN / 32;                    // weight fragments per plane and K-step
     static constexpr int A_ROWS = NA * BM;
-    static constexpr int B_ROWS = 3 * BN;
     static constexpr int A_LOADS = A_ROWS * 2 / kWave;   // 1 KB load instructions per stage
-    static constexpr int B_LOADS = B_ROWS * 2 / kWave;
-    static constexpr int STAGE = (A_ROWS + B_ROWS) * 32;  // bytes
-    static constexpr int NBUF = 2;
-    static constexpr size_t LDS = static_cast<size_t>(NBUF) * STAGE;
-    // when every wave issues the same number of loads per stage, a wave can
-    // wait for exactly its own loads of the oldest stage
-    static constexpr bool UNIFORM = (A_LOADS % kGemmWaves == 0) && (B_LOADS % kGemmWaves == 0);
-    static constexpr int PER_WAVE = (A_LOADS + B_LOADS) / kGemmWaves;
+    static constexpr int STAGE = A_ROWS * 32;            // bytes
+    static constexpr size_t LDS = static_cast<size_t>(kARing) * STAGE;
 };
 
-// s_waitcnt immediate that waits until at most `vm` vector-memory operations
-// of this wave are outstanding (gfx9 encoding; lgkm and exp counters untouched).
-template <int VM>
-constexpr int vmcnt_imm() {
-    return (VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
-// One stage of direct-to-LDS loads (K columns [k0, k0 + 16)) into the stage
-// buffer at `base`; input rows beyond T read the zero block; the weight tile
-// of (expert tile n_tile, K-step k0/16) is read as one contiguous block.
+// Input rows [m0, m0 + BM) x K columns [k0, k0 + 16) of every input plane into
+// the stage buffer at `base`; rows beyond T read the zero block.
 template <typename S>
-__device__ __forceinline__ void issue_stage(char* base, int k0, int kend, int wave, int lane, int m0,
-                                            int n_tile, int T, int H,
-                                            const uint16_t* __restrict__ a_planes, size_t a_plane,
-                                            const uint16_t* __restrict__ w_tiled,
-                                            const uint16_t* __restrict__ zero16) {
+__device__ __forceinline__ void issue_a(char* base, int k0, int wave, int lane, int m0, int T, int H,
+                                        const uint16_t* __restrict__ a_planes, size_t a_plane,
+                                        const uint16_t* __restrict__ zero16) {
     const int lr = lane >> 1;
     const int sc = lane & 1;
     for (int i = wave; i < S::A_LOADS; i += kGemmWaves) {
         const int R = i * 32 + lr;
         const int c = sc ^ swz(R);
         const int p = R / S::BM, r = R - p * S::BM;
-        const int row = m0 + r, k = k0 + c * 8;
-        const uint16_t* src = (row < T && k < kend)
-            ? a_planes + p * a_plane + static_cast<size_t>(row) * H + k : zero16;
+        const int row = m0 + r;
+        const uint16_t* src = row < T ? a_planes + p * a_plane + static_cast<size_t>(row) * H + k0 + c * 8 : zero16;
         __builtin_amdgcn_global_load_lds(src, base + i * 1024, 16, 0, 0);
     }
-    const uint16_t* blk = w_tiled + (static_cast<size_t>(n_tile) * (H / kKC) + k0 / kKC) * (S::B_LOADS * 512);
-    for (int i = wave; i < S::B_LOADS; i += kGemmWaves)
-        __builtin_amdgcn_global_load_lds(blk + i * 512 + lane * 8, base + S::A_ROWS * 32 + i * 1024, 16, 0, 0);
 }
 
 // Block b works on K-slice b % nsplit and tile b / nsplit. Blocks go to the
 // eight XCDs round-robin, so when nsplit divides 8 every XCD only ever reads
 // one K-slice of the weight planes and keeps it in its own L2.
 template <int NA, int MT, int NT>
-__global__ __launch_bounds__(kGemmBlock) void proj_kernel(
-    const uint16_t* __restrict__ a_planes, const uint16_t* __restrict__ w_planes,
+__global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2))) void proj_kernel(
+    const uint16_t* __restrict__ a_planes, const uint16_t* __restrict__ w_frags,
     const uint16_t* __restrict__ zero16, int T, int H, int E, int kslice, int nsplit,
     int tiles_m, float* __restrict__ partials) {
     using S = GemmShape<NA, MT, NT>;
-    constexpr int NBUF = S::NBUF;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x;
     const int lane = __lane_id();
@@ -200,8 +186,11 @@ __global__ __launch_bounds__(kGemmBlock) void proj_kernel(
     const int n0 = n_tile * S::BN;
     const int kbeg = split * kslice;
     const int kend = min(H, kbeg + kslice);
-    const int nstages = (kend - kbeg + kKC - 1) / kKC;
+    const int nst = (kend - kbeg) / kKC;
     const size_t a_plane = static_cast<size_t>(T) * H;
+    // this tile's fragments, from the first K-step of the slice
+    const bf16x8_t* frags = reinterpret_cast<const bf16x8_t*>(w_frags) +
+                            (static_cast<size_t>(n_tile) * (H / kKC) + kbeg / kKC) * (3 * S::G * kWave);
 
     f32x16_t acc[MT][NT];
 #pragma unroll
@@ -211,48 +200,55 @@ __global__ __launch_bounds__(kGemmBlock) void proj_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
-    const int frow = lane & 31;
-    const int c = lane >> 5;   // chunk: K columns [8c, 8c + 8) of the stage
-    for (int s = 0; s < NBUF - 1 && s < nstages; ++s)
-        issue_stage<S>(lds + s * S::STAGE, kbeg + s * kKC, kend, wave, lane, m0, n_tile, T, H,
-                       a_planes, a_plane, w_planes, zero16);
-    for (int s = 0; s < nstages; ++s) {
-        // wait for this wave's loads of stage s; the later stages may still fly
-        if (S::UNIFORM && NBUF > 2 && s + NBUF - 2 < nstages)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NBUF - 2) * S::PER_WAVE>());
-        else
-            __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();   // every wave's loads of stage s landed; buffer (s-1)%NBUF is free
-        if (s + NBUF - 1 < nstages)
-            issue_stage<S>(lds + ((s + NBUF - 1) % NBUF) * S::STAGE, kbeg + (s + NBUF - 1) * kKC, kend,
-                           wave, lane, m0, n_tile, T, H, a_planes, a_plane, w_planes, zero16);
-        const char* base = lds + (s % NBUF) * S::STAGE;
-        const char* bbase = base + S::A_ROWS * 32;
-        bf16x8_t a[NA][MT], b[3][NT];
-#pragma unroll
-        for (int p = 0; p < NA; ++p)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                a[p][mt] = *reinterpret_cast<const bf16x8_t*>(base + slot_bytes(p * S::BM + mt * 32 + frow, c));
+    bf16x8_t bq[2][3][NT];
+    auto load_b = [&](int s, bf16x8_t (&b)[3][NT]) {
+        const bf16x8_t* src = frags + static_cast<size_t>(s) * (3 * S::G * kWave);
 #pragma unroll
         for (int p = 0; p < 3; ++p)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                b[p][nt] = *reinterpret_cast<const bf16x8_t*>(
-                    bbase + slot_bytes(p * S::BN + wave * 32 * NT + nt * 32 + frow, c));
-        // products (input plane, weight plane) in the outer loop, so that
-        // consecutive MFMAs write different accumulators
-        constexpr int NPROD = NA == 1 ? 3 : 6;
-        constexpr int PA[6] = {0, 0, 0, 1, 1, 2};
-        constexpr int PB[6] = {0, 1, 2, 0, 1, 0};
+            for (int nt = 0; nt < NT; ++nt) b[p][nt] = src[(p * S::G + wave * NT + nt) * kWave + lane];
+    };
+
+    const int frow = lane & 31;
+    const int c = lane >> 5;   // chunk: K columns [8c, 8c + 8) of the step
+    if (nst > 0) load_b(0, bq[0]);
+    for (int s = 0; s < kARing - 1 && s < nst; ++s)
+        issue_a<S>(lds + s * S::STAGE, kbeg + s * kKC, wave, lane, m0, T, H, a_planes, a_plane, zero16);
+    for (int s0 = 0; s0 < nst; s0 += 2) {
 #pragma unroll
-        for (int q = 0; q < NPROD; ++q)
+        for (int ph = 0; ph < 2; ++ph) {
+            const int s = s0 + ph;
+            if (s < nst) {
+                // every load of this wave has landed (stage s included), then
+                // every wave's: stage s is complete and stage s-1 is free
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (s + 1 < nst) load_b(s + 1, bq[ph ^ 1]);
+                if (s + kARing - 1 < nst)
+                    issue_a<S>(lds + ((s + kARing - 1) % kARing) * S::STAGE, kbeg + (s + kARing - 1) * kKC,
+                               wave, lane, m0, T, H, a_planes, a_plane, zero16);
+                const char* base = lds + (s % kARing) * S::STAGE;
+                bf16x8_t a[NA][MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int p = 0; p < NA; ++p)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[q]][mt], b[PB[q]][nt],
-                                                                          acc[mt][nt], 0, 0, 0);
+                    for (int mt = 0; mt < MT; ++mt)
+                        a[p][mt] = *reinterpret_cast<const bf16x8_t*>(base + slot_bytes(p * S::BM + mt * 32 + frow, c));
+                // products (input plane, weight plane) in the outer loop, so
+                // that consecutive MFMAs write different accumulators
+                constexpr int NPROD = NA == 1 ? 3 : 6;
+                constexpr int PA[6] = {0, 0, 0, 1, 1, 2};
+                constexpr int PB[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+                for (int q = 0; q < NPROD; ++q)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[q]][mt], bq[ph][PB[q]][nt],
+                                                                                  acc[mt][nt], 0, 0, 0);
+            }
+        }
     }
 
     // 32x32 accumulator layout: lane holds column (lane & 31) and rows
@@ -263,7 +259,7 @@ __global__ __launch_bounds__(kGemmBlock) void proj_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int col = n0 + wave * 32 * NT + nt * 32 + (lane & 31);
+            const int col = n0 + (wave * NT + nt) * 32 + (lane & 31);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = m0 + mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -288,6 +284,7 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
     p.na = hidden_dtype == MOE_DTYPE_F32 ? 3 : 1;
     p.nt = E > 128 ? 2 : 1;
     p.mt = T >= 2048 ? 4 : (T >= 256 ? 2 : 1);
+    if (p.na == 3 && p.mt > 2) p.mt = 2;   // three input planes: keep the registers of two blocks per CU
     p.tiles_m = ceil_div(T, 32 * p.mt);
     p.tiles_n = ceil_div(E, 128 * p.nt);
     const int tiles = p.tiles_m * p.tiles_n;
@@ -298,7 +295,7 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
     p.kslice = per * kKC;
     p.nsplit = ceil_div(H, p.kslice);
     p.zero_bytes = 256;
-    // tiled planes, padded to whole expert tiles
+    // fragment-ordered planes, padded to whole expert tiles
     p.w_planes_bytes = round256(static_cast<size_t>(3) * p.tiles_n * 128 * p.nt * H * sizeof(uint16_t));
     p.a_planes_bytes = p.na == 3 ? round256(static_cast<size_t>(3) * T * H * sizeof(uint16_t)) : 0;
     p.partial_bytes = round256(static_cast<size_t>(p.nsplit) * T * E * sizeof(float));
@@ -309,7 +306,6 @@ template <int NA, int MT, int NT>
 int launch_proj(const RoutePlan& p, const uint16_t* a, const uint16_t* w, const uint16_t* zero,
                 int T, int H, int E, float* partials, void* stream) {
     using S = GemmShape<NA, MT, NT>;
-    static_assert(S::NBUF >= 2, "LDS too small for two stages");
     return launch(proj_kernel<NA, MT, NT>, dim3(p.tiles_m * p.tiles_n * p.nsplit), dim3(kGemmBlock),
                   S::LDS, stream, a, w, zero, T, H, E, p.kslice, p.nsplit, p.tiles_m, partials);
 }
@@ -319,7 +315,7 @@ int run_proj(const RoutePlan& p, const uint16_t* a, const uint16_t* w, const uin
 #define MOE_PROJ(NA, MT, NT) \
     if (p.na == NA && p.mt == MT && p.nt == NT) return launch_proj<NA, MT, NT>(p, a, w, zero, T, H, E, partials, stream);
     MOE_PROJ(1, 1, 1) MOE_PROJ(1, 1, 2) MOE_PROJ(1, 2, 1) MOE_PROJ(1, 2, 2) MOE_PROJ(1, 4, 1) MOE_PROJ(1, 4, 2)
-    MOE_PROJ(3, 1, 1) MOE_PROJ(3, 1, 2) MOE_PROJ(3, 2, 1) MOE_PROJ(3, 2, 2) MOE_PROJ(3, 4, 1) MOE_PROJ(3, 4, 2)
+    MOE_PROJ(3, 1, 1) MOE_PROJ(3, 1, 2) MOE_PROJ(3, 2, 1) MOE_PROJ(3, 2, 2)
 #undef MOE_PROJ
     return MOE_ERR_BAD_SHAPE;
 }
@@ -367,10 +363,10 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
     float* partials = reinterpret_cast<float*>(ws + p.zero_bytes + p.w_planes_bytes + p.a_planes_bytes);
 
     const int cap = device_cu_count() * 8;
-    const int bn = 128 * p.nt;
-    const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * 6 * bn;
+    const int G = 4 * p.nt;   // 32-expert groups per expert tile
+    const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * 3 * G * kWave;
     const int gw = ceil_div(wslots, 256);
-    int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, bn,
+    int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, G,
                     p.tiles_n, reinterpret_cast<u32x4*>(w_planes), reinterpret_cast<uint32_t*>(zero));
     if (rc) return rc;
     const uint16_t* a = static_cast<const uint16_t*>(hidden);

@@ -63,9 +63,12 @@ def test_pipeline_end_to_end(name, T):
     assert np.array_equal(r["scales"][rows][~near], rs[~near])
 
 
-def test_pipeline_graph_replay():
-    """Capture the four calls in a HIP graph and replay it with new inputs
-    copied into the captured buffers; every replay must equal the eager run."""
+@pytest.mark.parametrize("two_stream", [False, True])
+def test_pipeline_graph_replay(two_stream):
+    """Capture the four calls in a HIP graph -- on one stream, or with norm +
+    quant forked onto a second stream beside route -> dispatch -> combine --
+    and replay it with new inputs copied into the captured buffers; every
+    replay must equal a serial eager run bit for bit."""
     require_gpu()
     w = wl.WORKLOADS["decode"]
     T = w.T
@@ -85,12 +88,24 @@ def test_pipeline_graph_replay():
     packed = torch.empty((T, w.H // 2), dtype=torch.uint8, device=DEV)
     scales = torch.empty((T, w.H // 16), dtype=torch.uint8, device=DEV)
     out = torch.empty((T, w.H), dtype=torch.bfloat16, device=DEV)
+    aux = torch.cuda.Stream()
+
+    def norm_quant():
+        m.norm_quant_nvfp4(x_d, qw_d, 1.0, w.eps, gs_d, packed=packed, scales=scales)
 
     def step():
+        main = torch.cuda.current_stream()
+        if two_stream:
+            aux.wait_stream(main)
+            with torch.cuda.stream(aux):
+                norm_quant()
         m.route(h_d, W_d, b_d, m_d, w.k, logits=lg, topk_ids=ids, topk_w=tw, workspace=ws_r)
         m.dispatch(ids, w.E, counts=counts, offsets=offsets, perm=perm, dest=dest, workspace=ws_d)
-        m.norm_quant_nvfp4(x_d, qw_d, 1.0, w.eps, gs_d, packed=packed, scales=scales)
+        if not two_stream:
+            norm_quant()
         m.combine(eo_d, dest.view(T, w.k), tw, cg_d, 0.0, w.eps, out=out)
+        if two_stream:
+            main.wait_stream(aux)
 
     def snapshot():
         return [host(t).copy() for t in (lg, ids, tw, counts, offsets, perm, dest, packed, scales, out)]
@@ -107,7 +122,7 @@ def test_pipeline_graph_replay():
     torch.cuda.synchronize()
     g = np.random.default_rng(12)
     for rep in range(3):
-        note("graph replay %d" % rep)
+        note("graph replay %d (two_stream=%s)" % (rep, two_stream))
         # new inputs in place
         h_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
         x_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
@@ -117,7 +132,10 @@ def test_pipeline_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         replayed = snapshot()
+        two = two_stream
+        two_stream = False   # the eager reference runs serially on one stream
         step()
+        two_stream = two
         torch.cuda.synchronize()
         eager = snapshot()
         for a, b in zip(replayed, eager):
