@@ -1,7 +1,7 @@
 """Benchmark of the MoE routing-and-combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-                    [--schedule overlap|serial] [--no-graph]
+                    [--schedule overlap|serial] [--graph]
 
 One step is one pass of the whole path over one batch of synthetic input:
 moe_route -> moe_dispatch -> moe_combine, and moe_norm_quant_nvfp4, with
@@ -9,13 +9,15 @@ inputs resident in HBM and every output and workspace allocated before the
 timed region. The default workload is the 8192-token prefill batch (H=8192,
 E=256, k=8, 5% invalid tokens). Prints one JSON line.
 
-Schedules (the headline is the default, overlap + graph):
+Schedules (the headline is the default, overlap launched eagerly):
   serial   the four calls in order on one stream
   overlap  norm + quant on a second stream beside route -> dispatch ->
            combine (it depends on none of them); the step forks from the
            main stream and joins back into it, so it ends when both are done
-  graph    the step captured once in a HIP graph and replayed per step (no
-           per-launch host overhead); every kernel still runs every step
+  graph    the step captured once in a HIP graph and replayed per step;
+           every kernel still runs every step. Measured beside the headline:
+           on this stack the replay runs the forked branch serially and
+           comes out slower than the eager overlap
 
 Alongside the throughput the line carries:
   stages        per-call mean duration (HIP events on the launch stream, from
@@ -120,8 +122,8 @@ def main():
                     help="skip the 1 GiB device-copy reference bandwidth")
     ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
                     help="headline schedule: norm+quant beside the route on a second stream, or all on one")
-    ap.add_argument("--no-graph", dest="graph", action="store_false",
-                    help="launch the headline schedule eagerly instead of replaying a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the headline schedule from a HIP graph instead of launching it eagerly")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="serial steps timed after flushing the last-level cache (0: skip)")
     args = ap.parse_args()
@@ -252,6 +254,16 @@ def main():
     torch.cuda.synchronize()
     serial_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
     overlap_eager_ms = timed(step_overlap, args.steps)
+    if args.graph and args.schedule == "overlap":
+        overlap_graph_ms = ms_per_step
+    else:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            step_overlap()
+        torch.cuda.synchronize()
+        g2.replay()
+        overlap_graph_ms = timed(g2.replay, args.steps)
+        del g2
 
     # cold: flush the 256 MB last-level cache (a 512 MiB write) before each step
     cold_ms = None
@@ -267,6 +279,27 @@ def main():
         cold_ms = float(np.mean([a.elapsed_time(b) for a, b in ce]))
         del flush
 
+    # norm + quant reading the rank-block layout of 8 column shards
+    # ([8*T, H/8], what a dim-0 all-gather of the shards leaves)
+    rank_block = None
+    if H % (8 * 16) == 0:
+        tp = 8
+        pooled = x.view(T, tp, H // tp).transpose(0, 1).contiguous().view(tp * T, H // tp)
+        rb_packed, rb_scales = torch.empty_like(packed), torch.empty_like(scales)
+        m.norm_quant_nvfp4_rank_block(pooled, T, qw, w.quant_gain_center, w.eps, gs, packed=rb_packed, scales=rb_scales)
+        norm_quant_()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(rb_packed, packed) and torch.equal(rb_scales, scales))
+        re = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in re:
+            a.record(stream)
+            m.norm_quant_nvfp4_rank_block(pooled, T, qw, w.quant_gain_center, w.eps, gs, packed=rb_packed, scales=rb_scales)
+            b.record(stream)
+        torch.cuda.synchronize()
+        rb_ms = float(np.mean([a.elapsed_time(b) for a, b in re]))
+        rank_block = {"tp": tp, "ms": round(rb_ms, 4), "same_bytes_as_contiguous": same}
+        del pooled, rb_packed, rb_scales
+
     names = ["route", "dispatch", "norm_quant", "combine"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
@@ -276,6 +309,9 @@ def main():
     stages = {n: {"ms": round(stage_ms[n], 4), "bytes": nbytes[n],
                   "GBps": round(nbytes[n] / (stage_ms[n] * 1e-3) / 1e9, 1)} for n in names}
     proj_flop = 2.0 * T * H * E
+    if rank_block is not None:
+        rank_block["GBps"] = round(nbytes["norm_quant"] / (rank_block["ms"] * 1e-3) / 1e9, 1)
+        stages["norm_quant_rank_block"] = rank_block
     stages["route"]["proj_TFLOPs_fp32_equiv"] = round(proj_flop / (stage_ms["route"] * 1e-3) / 1e12, 2)
 
     comb_gbs = nbytes["combine"] / (stage_ms["combine"] * 1e-3) / 1e9
@@ -322,6 +358,7 @@ def main():
         "stages": stages,
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
                       "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
+                      "overlap_graph_ms": round(overlap_graph_ms, 4),
                       "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4)},
         "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),

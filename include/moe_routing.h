@@ -11,7 +11,9 @@
  *                         permutation of the routed slots by expert
  *   moe_norm_quant_nvfp4  RMSNorm of the expert input with one BF16 rounding,
  *                         fused with NVFP4 quantisation (E2M1 codes, E4M3
- *                         block-16 scales, static global scale)
+ *                         block-16 scales, static global scale); the
+ *                         _rank_block variant reads the input in the
+ *                         [tp*T, H/tp] layout a column all-gather leaves
  *   moe_combine           per-row RMSNorm of each selected expert output,
  *                         routing-weight scaling and top-k sum; invalid slots
  *                         are never read
@@ -171,6 +173,29 @@ int moe_dispatch(const int32_t* topk_ids, int T, int k, int E,
 int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, float gain_center, float eps,
                          const float* global_scale, int T, int H,
                          uint8_t* packed, uint8_t* scales, void* stream);
+
+/*
+ * moe_norm_quant_nvfp4_rank_block — the same operation on input in the
+ * rank-block layout.
+ *
+ * Defined by the vLLM API docs of vllm.models.muse_spark.nvidia.ops.
+ * prepare_trtllm_nvfp4 (module description and `norm_quant_trtllm_nvfp4`):
+ * the pooled input is either [M, H] or the [tp * M, H / tp] result of a
+ * dim-0 all-gather of column shards, i.e. tp blocks of [M, H / tp], block r
+ * holding columns [r * shard, (r + 1) * shard) of every row.
+ *
+ *   x      [H/shard * T, shard] BF16 bits: element (t, i) of the logical
+ *          [T,H] input is x[(i / shard) * T + t, i % shard].
+ *   shard  columns per rank block: 16 <= shard <= H, shard % 16 == 0 (an
+ *          NVFP4 block never straddles two shards) and H % shard == 0.
+ *          shard == H is the contiguous layout and gives moe_norm_quant_nvfp4.
+ *   Every other argument, the outputs (packed and scales in the logical
+ *   [T, ...] layout) and the errors are those of moe_norm_quant_nvfp4;
+ *   a shard outside these rules is BAD_SHAPE.
+ */
+int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, const float* norm_w,
+                                    float gain_center, float eps, const float* global_scale,
+                                    int T, int H, uint8_t* packed, uint8_t* scales, void* stream);
 
 /*
  * moe_combine — post-expert RMSNorm, weighting and top-k sum.

@@ -38,6 +38,8 @@ _SIGNATURES = {
     "moe_dispatch_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_dispatch": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_norm_quant_nvfp4": (_c_int, [_vp, _vp, _c_float, _c_float, _vp, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_norm_quant_nvfp4_rank_block": (_c_int, [_vp, _c_int, _vp, _c_float, _c_float, _vp, _c_int, _c_int,
+                                                 _vp, _vp, _vp]),
     "moe_combine": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_float, _c_float, _c_int, _c_int, _c_int,
                              _vp, _vp]),
 }
@@ -188,6 +190,35 @@ def norm_quant_nvfp4(x: torch.Tensor, norm_w: torch.Tensor, gain_center: float, 
     if x.dim() != 2:
         raise ValueError("x must be [T,H]")
     T, H = x.shape
+    packed, scales = _norm_quant_outputs(norm_w, global_scale, T, H, packed, scales, dev)
+    _check("moe_norm_quant_nvfp4", lib().moe_norm_quant_nvfp4(
+        _ptr(x), _ptr(norm_w), float(gain_center), float(eps), _ptr(global_scale), T, H,
+        _ptr(packed), _ptr(scales), _stream(dev)))
+    return packed, scales
+
+
+def norm_quant_nvfp4_rank_block(x: torch.Tensor, num_tokens: int, norm_w: torch.Tensor, gain_center: float,
+                                eps: float, global_scale: torch.Tensor, *, packed=None, scales=None):
+    """moe_norm_quant_nvfp4_rank_block. x is [tp * T, H / tp] bf16 (tp blocks
+    of column shards stacked along dim 0; tp = 1 is the contiguous [T,H]);
+    H is norm_w's length. Returns (packed [T,H/2], scales [T,H/16])."""
+    dev = x.device
+    _need(x, "x", _BF16, None, dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [tp*T, H/tp]")
+    T = int(num_tokens)
+    H = norm_w.shape[0] if norm_w.dim() == 1 else -1
+    shard = x.shape[1]
+    if T < 0 or H <= 0 or x.shape[0] * shard != T * H:
+        raise ValueError("x holds %d x %d values, not num_tokens * H = %d * %d" % (x.shape[0], shard, T, H))
+    packed, scales = _norm_quant_outputs(norm_w, global_scale, T, H, packed, scales, dev)
+    _check("moe_norm_quant_nvfp4_rank_block", lib().moe_norm_quant_nvfp4_rank_block(
+        _ptr(x), shard, _ptr(norm_w), float(gain_center), float(eps), _ptr(global_scale), T, H,
+        _ptr(packed), _ptr(scales), _stream(dev)))
+    return packed, scales
+
+
+def _norm_quant_outputs(norm_w, global_scale, T, H, packed, scales, dev):
     _need(norm_w, "norm_w", (torch.float32,), (H,), dev)
     _need(global_scale, "global_scale", (torch.float32,), None, dev)
     if global_scale.numel() != 1:
@@ -196,9 +227,6 @@ def norm_quant_nvfp4(x: torch.Tensor, norm_w: torch.Tensor, gain_center: float, 
     scales = torch.empty((T, H // 16), dtype=torch.uint8, device=dev) if scales is None else scales
     _need(packed, "packed", (torch.uint8,), (T, H // 2), dev)
     _need(scales, "scales", (torch.uint8,), (T, H // 16), dev)
-    _check("moe_norm_quant_nvfp4", lib().moe_norm_quant_nvfp4(
-        _ptr(x), _ptr(norm_w), float(gain_center), float(eps), _ptr(global_scale), T, H,
-        _ptr(packed), _ptr(scales), _stream(dev)))
     return packed, scales
 
 

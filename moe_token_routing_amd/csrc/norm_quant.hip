@@ -8,6 +8,11 @@
 // reciprocals); TensorRT-LLM PR #21356, description, "Numerics" (gain centre
 // added in FP32, the norm rounds only its result).
 //
+// The input may also be in the rank-block layout [tp*T, H/tp] that a dim-0
+// all-gather of column shards leaves (same docs, module description): each
+// thread's vectors keep their rank block for every token, so the layout only
+// changes a per-thread row offset computed once.
+//
 // Design (gfx950): one HBM pass. A row is read once with 16-byte loads into
 // registers; its sum of squares is reduced across the token's threads; each
 // 16-element block is two neighbouring 8-element vectors held by adjacent
@@ -92,8 +97,8 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t word, uint32_t ypair, floa
 template <int VPT>
 __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
-    const float* __restrict__ global_scale, int T, int H, int tpt, uint32_t* __restrict__ packed,
-    uint8_t* __restrict__ scales) {
+    const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
+    uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
     __shared__ float red[kRowBlock / kWave];
     const int nvec = H >> 3;
     const int tokens_per_block = kRowBlock / tpt;
@@ -105,9 +110,14 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     constexpr float kRcp6 = 1.0f / 6.0f;
 
     float gain[VPT][8];
+    // vector v (logical columns [8v, 8v+8)) of token t sits at
+    // src[i] + t * shard8 (16-byte units), rank block v / shard8
+    size_t src[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int v = tid + i * tpt;
+        const int rb = v / shard8;
+        src[i] = static_cast<size_t>(rb) * T * shard8 + (v - rb * shard8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) gain[i][e] = 0.f;
         if (v < nvec) {
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
         for (int i = 0; i < VPT; ++i) {
             const int v = tid + i * tpt;
             xv[i] = u32x4{0u, 0u, 0u, 0u};
-            if (tok_ok && v < nvec) xv[i] = load_nt(&x[static_cast<size_t>(t) * nvec + v]);
+            if (tok_ok && v < nvec) xv[i] = load_nt(&x[src[i] + static_cast<size_t>(t) * shard8]);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
 
 template <int VPT>
 int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
-                      const float* global_scale, int T, int H, const RowGeom& geo,
+                      const float* global_scale, int T, int H, int shard, const RowGeom& geo,
                       uint8_t* packed, uint8_t* scales, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
@@ -199,17 +209,19 @@ int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center,
     const int grid = needed < cap ? needed : cap;
     return launch(norm_quant_kernel<VPT>, dim3(grid), dim3(kRowBlock), 0, stream,
                   reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
-                  geo.tpt, reinterpret_cast<uint32_t*>(packed), scales);
+                  shard / 8, geo.tpt, reinterpret_cast<uint32_t*>(packed), scales);
 }
 
 }  // namespace
 }  // namespace moe
 
-extern "C" int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, float gain_center,
-                                    float eps, const float* global_scale, int T, int H,
-                                    uint8_t* packed, uint8_t* scales, void* stream) {
+extern "C" int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, const float* norm_w,
+                                               float gain_center, float eps, const float* global_scale,
+                                               int T, int H, uint8_t* packed, uint8_t* scales,
+                                               void* stream) {
     using namespace moe;
     if (T < 0 || H < 16 || H > MOE_MAX_HIDDEN || H % 16 != 0) return MOE_ERR_BAD_SHAPE;
+    if (shard < 16 || shard > H || shard % 16 != 0 || H % shard != 0) return MOE_ERR_BAD_SHAPE;
     if (!std::isfinite(gain_center) || !std::isfinite(eps) || eps < 0.f) return MOE_ERR_BAD_ARG;
     if (T == 0) return MOE_OK;
     if (!x || !norm_w || !global_scale || !packed || !scales) return MOE_ERR_NULL_ARG;
@@ -218,10 +230,18 @@ extern "C" int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, floa
     int vpt = 1;
     while (vpt < geo.vpt) vpt <<= 1;
     switch (vpt) {
-        case 1: return launch_norm_quant<1>(x, norm_w, gain_center, eps, global_scale, T, H, geo, packed, scales, stream);
-        case 2: return launch_norm_quant<2>(x, norm_w, gain_center, eps, global_scale, T, H, geo, packed, scales, stream);
-        case 4: return launch_norm_quant<4>(x, norm_w, gain_center, eps, global_scale, T, H, geo, packed, scales, stream);
-        case 8: return launch_norm_quant<8>(x, norm_w, gain_center, eps, global_scale, T, H, geo, packed, scales, stream);
+        case 1: return launch_norm_quant<1>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
+        case 2: return launch_norm_quant<2>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
+        case 4: return launch_norm_quant<4>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
+        case 8: return launch_norm_quant<8>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
         default: return MOE_ERR_BAD_SHAPE;
     }
+}
+
+extern "C" int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, float gain_center,
+                                    float eps, const float* global_scale, int T, int H,
+                                    uint8_t* packed, uint8_t* scales, void* stream) {
+    if (H < 16 || H % 16 != 0) return MOE_ERR_BAD_SHAPE;
+    return moe_norm_quant_nvfp4_rank_block(x, H, norm_w, gain_center, eps, global_scale, T, H, packed,
+                                           scales, stream);
 }

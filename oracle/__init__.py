@@ -23,7 +23,8 @@ from .route import (router_logits, sigmoid_f32, selection_keys, topk_sorted,
                     renormalized_weights, route_from_logits, route, key_gap_near_ties)
 from .dispatch import dispatch
 from .nvfp4 import (gain_f32, rmsnorm_exact, rmsnorm_bf16, nvfp4_quantize,
-                    norm_quant_nvfp4, global_scale, midpoint_boundary_blocks, dequantize)
+                    norm_quant_nvfp4, global_scale, midpoint_boundary_blocks, dequantize,
+                    rank_block_rows, norm_quant_nvfp4_rank_block)
 from .combine import combine
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -9,7 +9,10 @@ Source: vLLM API docs, vllm.models.muse_spark.nvidia.ops.prepare_trtllm_nvfp4:
     [M, H/16] E4M3 scales; H must be a multiple of the block; M = 0 returns
     at once; the kernel runs without FP contraction;
   - `_quantize_nvfp4_global_scale`: the per-16-element block arithmetic, whose
-    steps this module takes in the same order.
+    steps this module takes in the same order;
+  - module text and `norm_quant_trtllm_nvfp4`'s docstring: the input may
+    instead be the [tp * M, H / tp] result of a dim-0 all-gather of column
+    shards (the rank-block layout), read as the same logical [M, H] rows.
 Also TensorRT-LLM PR #21356, "Add the Muse Spark Open decoder fast paths",
 description, "Numerics": the norm adds the 1 (gain centre) to the weight in
 FP32 and rounds only its result.
@@ -87,6 +90,24 @@ def norm_quant_nvfp4(x_bits, norm_w, gain_center, eps, global_scale):
     """RMSNorm (one BF16 rounding) followed by NVFP4 quantisation."""
     y = rmsnorm_bf16(x_bits, norm_w, gain_center, eps)
     return nvfp4_quantize(y, global_scale)
+
+
+def rank_block_rows(pooled: np.ndarray, num_tokens: int, hidden: int) -> np.ndarray:
+    """The logical [M, H] rows of a rank-block input [tp * M, H / tp]: block r
+    (rows r*M .. r*M + M - 1) holds columns r*S .. r*S + S - 1 of every row,
+    S = H / tp (prepare_trtllm_nvfp4, `norm_quant_trtllm_nvfp4`). tp = 1 is the
+    contiguous layout."""
+    pooled = np.asarray(pooled)
+    M, S = int(num_tokens), pooled.shape[1]
+    assert pooled.shape[0] * S == M * hidden and hidden % S == 0
+    tp = hidden // S
+    return pooled.reshape(tp, M, S).transpose(1, 0, 2).reshape(M, hidden)
+
+
+def norm_quant_nvfp4_rank_block(pooled_bits, num_tokens, norm_w, gain_center, eps, global_scale):
+    """norm_quant_nvfp4 of the logical rows of a rank-block input."""
+    x = rank_block_rows(pooled_bits, num_tokens, np.asarray(norm_w).shape[0])
+    return norm_quant_nvfp4(x, norm_w, gain_center, eps, global_scale)
 
 
 def global_scale(y: np.ndarray) -> np.float32:

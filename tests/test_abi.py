@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"moe_status_string", "moe_route_workspace_bytes", "moe_route",
                           "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_norm_quant_nvfp4",
-                          "moe_combine"}
+                          "moe_norm_quant_nvfp4_rank_block", "moe_combine"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(m._SIGNATURES)
@@ -83,6 +83,17 @@ def test_norm_quant_rejects_before_launch(lib):
     assert f(FAKE, FAKE, 1.0, 1e-6, None, 4, 64, FAKE, FAKE, None) == -1
     assert f(None, FAKE, 1.0, 1e-6, FAKE, 4, 64, FAKE, FAKE, None) == -1
     assert f(FAKE, FAKE, 1.0, 1e-6, FAKE, 0, 64, None, None, None) == 0
+
+
+def test_norm_quant_rank_block_rejects_before_launch(lib):
+    f = lib.moe_norm_quant_nvfp4_rank_block
+    assert f(FAKE, 24, FAKE, 1.0, 1e-6, FAKE, 4, 96, FAKE, FAKE, None) == -2    # shard % 16
+    assert f(FAKE, 64, FAKE, 1.0, 1e-6, FAKE, 4, 96, FAKE, FAKE, None) == -2    # H % shard
+    assert f(FAKE, 192, FAKE, 1.0, 1e-6, FAKE, 4, 96, FAKE, FAKE, None) == -2   # shard > H
+    assert f(FAKE, 0, FAKE, 1.0, 1e-6, FAKE, 4, 96, FAKE, FAKE, None) == -2
+    assert f(FAKE, 48, FAKE, 1.0, -1.0, FAKE, 4, 96, FAKE, FAKE, None) == -5
+    assert f(None, 48, FAKE, 1.0, 1e-6, FAKE, 4, 96, FAKE, FAKE, None) == -1
+    assert f(FAKE, 48, FAKE, 1.0, 1e-6, FAKE, 0, 96, None, None, None) == 0
 
 
 def test_route_rejects_before_launch(lib):

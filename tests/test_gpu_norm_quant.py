@@ -104,3 +104,47 @@ def test_norm_quant_zero_tokens():
                               torch.ones(64, dtype=torch.float32, device="cuda:0"), 1.0, 1e-6,
                               scalar_dev(1.0))
     assert p.shape == (0, 32) and s.shape == (0, 4)
+
+
+def _gather_shards(x, tp):
+    """The rank-block input a dim-0 all-gather of tp column shards leaves."""
+    S = x.shape[1] // tp
+    return np.ascontiguousarray(np.concatenate([x[:, r * S:(r + 1) * S] for r in range(tp)], axis=0))
+
+
+@pytest.mark.parametrize("name,T,tp", [("prefill", 300, 2), ("prefill", 300, 8), ("prefill", 64, 512),
+                                       ("wide_k", 1001, 4), ("wide_k", 1001, 64), ("tiny", None, 4)])
+def test_norm_quant_rank_block(name, T, tp):
+    """Rank-block input [tp*T, H/tp]: identical bytes to the contiguous call
+    on the same logical rows, and the oracle's parity rule on them."""
+    require_gpu()
+    w = wl.WORKLOADS[name]
+    T = w.T if T is None else T
+    x = wl.quant_input(w, T)
+    nw = wl.quant_gain(w)
+    y = O.rmsnorm_bf16(x, nw, w.quant_gain_center, w.eps)
+    gs = O.global_scale(y)
+    pooled = _gather_shards(x, tp)
+    note("norm_quant rank block %s T=%d H=%d tp=%d" % (name, T, w.H, tp))
+    p, s = m.norm_quant_nvfp4_rank_block(dev(pooled), T, dev(nw), w.quant_gain_center, w.eps, scalar_dev(gs))
+    torch.cuda.synchronize()
+    p, s = host(p), host(s)
+    pc, sc = _run(x, nw, w.quant_gain_center, w.eps, gs, name + " contiguous")
+    assert np.array_equal(p, pc) and np.array_equal(s, sc)
+    _check(x, nw, w.quant_gain_center, w.eps, gs, p, s, np.arange(T), name + " rank block")
+
+
+def test_norm_quant_rank_block_full_prefill_sampled():
+    """The prefill batch (T=8192, H=8192) as an 8-way rank block, sampled rows
+    against the oracle."""
+    require_gpu()
+    w = wl.WORKLOADS["prefill"]
+    x = wl.quant_input(w)
+    nw = wl.quant_gain(w)
+    gs = np.float32(345.4457702636719)
+    pooled = _gather_shards(x, 8)
+    note("norm_quant rank block prefill full tp=8")
+    p, s = m.norm_quant_nvfp4_rank_block(dev(pooled), w.T, dev(nw), w.quant_gain_center, w.eps, scalar_dev(gs))
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(7).choice(w.T, 64, replace=False)
+    _check(x, nw, w.quant_gain_center, w.eps, gs, host(p), host(s), np.sort(rows), "prefill rank block")

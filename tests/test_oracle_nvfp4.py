@@ -1,7 +1,8 @@
 """Pins of the RMSNorm + NVFP4 oracle: power-of-two rows that make the norm
 exact, the printed code thresholds reached through the public function,
 scale saturation and underflow, the quantisation error bound, and the
-variance taken over x rather than gain * x."""
+variance taken over x rather than gain * x; the rank-block input layout
+rebuilt from the column shards and dim-0 gather that define it."""
 import os
 
 import numpy as np
@@ -135,3 +136,36 @@ def test_boundary_blocks_flag_midpoints():
     np.testing.assert_array_equal(near, [[True, False]])
     near = O.midpoint_boundary_blocks(x, gain, 0.0, 0.0)
     assert not near.any()
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8])
+def test_rank_block_layout_is_the_gathered_column_shards(tp):
+    """The rank-block input is what a dim-0 all-gather of column shards
+    leaves (prepare_trtllm_nvfp4, `norm_quant_trtllm_nvfp4`): build it that
+    way -- each rank keeps columns [r*S, (r+1)*S) of every row, the ranks'
+    pieces are stacked along dim 0 -- and read it back, both through the
+    oracle and element by element by the stacking rule."""
+    M, H = 5, 128
+    g = np.random.default_rng(40 + tp)
+    x = g.integers(0, 1 << 16, size=(M, H), dtype=np.uint16)
+    S = H // tp
+    pooled = np.concatenate([x[:, r * S:(r + 1) * S] for r in range(tp)], axis=0)
+    assert pooled.shape == (tp * M, S)
+    assert np.array_equal(O.rank_block_rows(pooled, M, H), x)
+    for t in range(M):
+        for i in range(H):
+            assert pooled[(i // S) * M + t, i % S] == x[t, i]
+
+
+def test_rank_block_quant_matches_contiguous():
+    w = wl.WORKLOADS["wide_k"]
+    M, H = 9, w.H
+    x = wl.quant_input(w, M)
+    nw = wl.quant_gain(w)
+    gs = np.float32(3.0)
+    ref = O.norm_quant_nvfp4(x, nw, w.quant_gain_center, w.eps, gs)
+    for tp in (2, 8):
+        S = H // tp
+        pooled = np.concatenate([x[:, r * S:(r + 1) * S] for r in range(tp)], axis=0)
+        got = O.norm_quant_nvfp4_rank_block(pooled, M, nw, w.quant_gain_center, w.eps, gs)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
