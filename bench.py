@@ -1,7 +1,7 @@
 """Benchmark of the MoE routing-and-combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-                    [--schedule overlap|serial] [--graph]
+                    [--schedule overlap|overlap-route|serial] [--graph]
 
 One step is one pass of the whole path over one batch of synthetic input:
 moe_route -> moe_dispatch -> moe_combine, and moe_norm_quant_nvfp4, with
@@ -10,14 +10,17 @@ timed region. The default workload is the 8192-token prefill batch (H=8192,
 E=256, k=8, 5% invalid tokens). Prints one JSON line.
 
 Schedules (the headline is the default, overlap launched eagerly):
-  serial   the four calls in order on one stream
-  overlap  norm + quant on a second stream beside route -> dispatch ->
-           combine (it depends on none of them); the step forks from the
-           main stream and joins back into it, so it ends when both are done
-  graph    the step captured once in a HIP graph and replayed per step;
-           every kernel still runs every step. Measured beside the headline:
-           on this stack the replay runs the forked branch serially and
-           comes out slower than the eager overlap
+  serial         the four calls in order on one stream
+  overlap        route on the main stream, then norm + quant forked onto a
+                 second stream beside dispatch -> combine (it depends on none
+                 of them); the step joins back into the main stream, so it
+                 ends when both are done
+  overlap-route  norm + quant forked beside the route instead; the projection
+                 is power-bound, so the two mostly slow each other down
+  graph          the overlap step captured once in a HIP graph and replayed;
+                 every kernel still runs every step. On this stack the replay
+                 runs the forked branch serially and is slower than the eager
+                 overlap, so it is reported, not used
 
 Alongside the throughput the line carries:
   stages        per-call mean duration (HIP events on the launch stream, from
@@ -113,15 +116,16 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
                     help="skip the 1 GiB device-copy reference bandwidth")
-    ap.add_argument("--schedule", choices=["overlap", "serial"], default="overlap",
-                    help="headline schedule: norm+quant beside the route on a second stream, or all on one")
+    ap.add_argument("--schedule", choices=["overlap", "overlap-route", "serial"], default="overlap",
+                    help="headline schedule: norm+quant on a second stream beside dispatch + combine "
+                         "(overlap) or beside the route (overlap-route), or all on one stream (serial)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline schedule from a HIP graph instead of launching it eagerly")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -202,7 +206,7 @@ def main():
 
     aux = torch.cuda.Stream(device=dev)   # default priority
 
-    def step_overlap():
+    def step_overlap_route():
         main = torch.cuda.current_stream(dev)
         aux.wait_stream(main)              # fork
         with torch.cuda.stream(aux):
@@ -212,6 +216,18 @@ def main():
         combine_()
         main.wait_stream(aux)              # join: the step ends when both are done
 
+    def step_overlap():
+        # the projection is power-bound, so norm + quant goes beside the
+        # latency-bound dispatch and the combine rather than beside it
+        main = torch.cuda.current_stream(dev)
+        route_()
+        aux.wait_stream(main)              # fork
+        with torch.cuda.stream(aux):
+            norm_quant_()
+        dispatch_()
+        combine_()
+        main.wait_stream(aux)              # join
+
     def timed(fn, steps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -220,7 +236,7 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1000.0 / steps
 
-    head_step = step_overlap if args.schedule == "overlap" else step_serial
+    head_step = {"overlap": step_overlap, "overlap-route": step_overlap_route, "serial": step_serial}[args.schedule]
     # warm up eagerly on a side stream (as graph capture requires), then capture
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(stream)
@@ -242,7 +258,9 @@ def main():
 
     # headline: exactly K steps between two synchronizations
     ms_per_step = timed(head_fn, args.steps)
-    head_name = ("two-stream overlap" if args.schedule == "overlap" else "serial") + \
+    head_name = {"overlap": "norm+quant on a second stream beside dispatch + combine",
+                 "overlap-route": "norm+quant on a second stream beside the route",
+                 "serial": "serial"}[args.schedule] + \
         (", HIP graph replay" if args.graph else ", eager launches")
 
     # serial eager pass with per-call events on the launch stream
@@ -254,6 +272,7 @@ def main():
     torch.cuda.synchronize()
     serial_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
     overlap_eager_ms = timed(step_overlap, args.steps)
+    overlap_route_ms = timed(step_overlap_route, args.steps)
     if args.graph and args.schedule == "overlap":
         overlap_graph_ms = ms_per_step
     else:
@@ -358,6 +377,7 @@ def main():
         "stages": stages,
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
                       "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
+                      "overlap_route_eager_ms": round(overlap_route_ms, 4),
                       "overlap_graph_ms": round(overlap_graph_ms, 4),
                       "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4)},
         "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),

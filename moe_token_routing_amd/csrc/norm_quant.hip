@@ -14,10 +14,11 @@
 // changes a per-thread row offset computed once.
 //
 // Design (gfx950): one HBM pass. A row is read once with 16-byte loads into
-// registers; its sum of squares is reduced across the token's threads; each
-// 16-element block is two neighbouring 8-element vectors held by adjacent
-// lanes, so the block maximum is one lane swap. Codes leave as one 32-bit
-// store per 8 elements, scales as one byte per block.
+// registers; its sum of squares is reduced across the token's threads. Each
+// lane owns whole 16-element blocks (two neighbouring vectors), so a block's
+// maximum, E4M3 scale (hardware FP8 conversion, clamped to saturate) and
+// reciprocal are computed once, and its 16 codes (hardware FP4 conversion)
+// leave as one 8-byte store, its scale as one byte.
 #include <cmath>
 
 #include "launch.hpp"
@@ -28,39 +29,6 @@ namespace {
 
 __device__ __forceinline__ float round_to_bf16(float f) {
     return __uint_as_float(f32_to_bf16_rne(f) << 16);
-}
-
-// E4M3 (no infinities, max 448): nearest value, ties to even code, magnitudes
-// above 448 saturate, NaN -> 0x7F. Works on |s| and puts the sign in bit 7.
-__device__ __forceinline__ uint32_t e4m3_satfinite(float s) {
-    if (!(s == s)) return 0x7Fu;
-    const uint32_t sign = (__float_as_uint(s) >> 24) & 0x80u;
-    const float a = fabsf(s);
-    uint32_t code;
-    if (a >= 448.f) {
-        code = 0x7Eu;
-    } else if (a < 0x1p-6f) {
-        // subnormal range: multiples of 2^-9; 8 * 2^-9 = 2^-6 is code 0x08
-        code = static_cast<uint32_t>(rintf(a * 512.f));
-    } else {
-        const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6..8
-        const float m = ldexpf(a, -e);                                            // [1, 2)
-        code = static_cast<uint32_t>((e + 7) << 3) + static_cast<uint32_t>(rintf((m - 1.f) * 8.f));
-    }
-    return code | sign;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    const uint32_t mag = c & 0x7Fu;
-    float v;
-    if (mag == 0x7Fu) {
-        v = __uint_as_float(0x7FC00000u);
-    } else {
-        const uint32_t e = mag >> 3, m = mag & 7u;
-        v = e == 0 ? static_cast<float>(m) * 0x1p-9f
-                   : ldexpf(static_cast<float>(8u + m), static_cast<int>(e) - 10);
-    }
-    return (c & 0x80u) ? -v : v;
 }
 
 // FP4 E2M1 code: magnitude rounded to the nearest of {0,.5,1,1.5,2,3,4,6}
@@ -94,13 +62,27 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t word, uint32_t ypair, floa
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, BYTE);
 }
 
-template <int VPT>
+// E4M3 byte of a block scale s >= 0 (or NaN): v_cvt_pk_fp8_f32 rounds to the
+// nearest E4M3 value with ties to the even code, subnormals included, but
+// turns magnitudes past 464 into NaN; clamping to 448 first gives the
+// saturating conversion, and NaN keeps the NaN code 0x7F.
+__device__ __forceinline__ uint32_t e4m3_scale_code(float s) {
+    if (!(s == s)) return 0x7Fu;
+    const float c = s > 448.f ? 448.f : s;
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false)) & 0xFFu;
+}
+
+// One lane quantises whole 16-element blocks: block b of a row is two
+// neighbouring 16-byte vectors, so its scale is computed once, by the lane
+// that holds it. A 256-thread block serves 256 / tpt tokens, tpt threads per
+// token (tpt = the power of two >= H/16, at most 256), BPT blocks per thread.
+template <int BPT>
 __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
     const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
-    uint32_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+    uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     __shared__ float red[kRowBlock / kWave];
-    const int nvec = H >> 3;
+    const int nblk = H >> 4;
     const int tokens_per_block = kRowBlock / tpt;
     const int sub = threadIdx.x / tpt;
     const int tid = threadIdx.x - sub * tpt;
@@ -108,108 +90,132 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const float gs = *global_scale;
     const float rcp_gs = 1.0f / gs;
     constexpr float kRcp6 = 1.0f / 6.0f;
-
-    float gain[VPT][8];
-    // vector v (logical columns [8v, 8v+8)) of token t sits at
-    // src[i] + t * shard8 (16-byte units), rank block v / shard8
-    size_t src[VPT];
+    // gains of this thread's blocks, and where block b of token t starts:
+    // src[i] + t * shard8 (16-byte units; both vectors of a block lie in one
+    // rank block since shard % 16 == 0)
+    float gain[BPT][16];
+    size_t src[BPT];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int v = tid + i * tpt;
+    for (int i = 0; i < BPT; ++i) {
+        const int b = tid + i * tpt;
+        const int v = 2 * b;
         const int rb = v / shard8;
         src[i] = static_cast<size_t>(rb) * T * shard8 + (v - rb * shard8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gain[i][e] = 0.f;
-        if (v < nvec) {
-            const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
-            const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
-            gain[i][0] = gain_center + a.x; gain[i][1] = gain_center + a.y;
-            gain[i][2] = gain_center + a.z; gain[i][3] = gain_center + a.w;
-            gain[i][4] = gain_center + b.x; gain[i][5] = gain_center + b.y;
-            gain[i][6] = gain_center + b.z; gain[i][7] = gain_center + b.w;
+        for (int e = 0; e < 16; ++e) gain[i][e] = 0.f;
+        if (b < nblk) {
+            const float4* g4 = reinterpret_cast<const float4*>(norm_w) + 4 * b;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a = g4[q];
+                gain[i][4 * q] = gain_center + a.x;
+                gain[i][4 * q + 1] = gain_center + a.y;
+                gain[i][4 * q + 2] = gain_center + a.z;
+                gain[i][4 * q + 3] = gain_center + a.w;
+            }
         }
     }
 
     for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
         const int t = t0 + sub;
         const bool tok_ok = t < T;
-        u32x4 xv[VPT];
+        uint32_t xw[BPT][8];   // block i: 16 BF16 values as 8 packed pairs
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            u32x4 a = u32x4{0u, 0u, 0u, 0u}, c = u32x4{0u, 0u, 0u, 0u};
+            if (tok_ok && tid + i * tpt < nblk) {
+                const u32x4* p = &x[src[i] + static_cast<size_t>(t) * shard8];
+                a = load_nt(p);
+                c = load_nt(p + 1);
+            }
+            xw[i][0] = a.x; xw[i][1] = a.y; xw[i][2] = a.z; xw[i][3] = a.w;
+            xw[i][4] = c.x; xw[i][5] = c.y; xw[i][6] = c.z; xw[i][7] = c.w;
+        }
         float ss[1] = {0.f};
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * tpt;
-            xv[i] = u32x4{0u, 0u, 0u, 0u};
-            if (tok_ok && v < nvec) xv[i] = load_nt(&x[src[i] + static_cast<size_t>(t) * shard8]);
-        }
+        for (int i = 0; i < BPT; ++i)
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            ss[0] = dot2_sq(xv[i].x, ss[0]);
-            ss[0] = dot2_sq(xv[i].y, ss[0]);
-            ss[0] = dot2_sq(xv[i].z, ss[0]);
-            ss[0] = dot2_sq(xv[i].w, ss[0]);
-        }
+            for (int q = 0; q < 8; ++q) ss[0] = dot2_sq(xw[i][q], ss[0]);
         token_sum(ss, tpt, red);
         const float rinv = 1.0f / sqrtf(ss[0] / hf + eps);
-
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * tpt;
-            const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        for (int i = 0; i < BPT; ++i) {
+            const int b = tid + i * tpt;
             // normalised pairs, rounded once to BF16 (packed)
-            uint32_t yp[4];
+            uint32_t yp[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                yp[q] = cvt_pk_bf16((bf16_lo(w4[q]) * gain[i][2 * q]) * rinv,
-                                    (bf16_hi(w4[q]) * gain[i][2 * q + 1]) * rinv);
+            for (int q = 0; q < 8; ++q)
+                yp[q] = cvt_pk_bf16((bf16_lo(xw[i][q]) * gain[i][2 * q]) * rinv,
+                                    (bf16_hi(xw[i][q]) * gain[i][2 * q + 1]) * rinv);
             // block maximum of |y|: the magnitude bits of non-negative BF16
             // values order like integers, and a NaN magnitude exceeds inf.
-            const uint32_t m01 = packed_max_u16(yp[0] & 0x7FFF7FFFu, yp[1] & 0x7FFF7FFFu);
-            const uint32_t m23 = packed_max_u16(yp[2] & 0x7FFF7FFFu, yp[3] & 0x7FFF7FFFu);
-            const uint32_t m = packed_max_u16(m01, m23);
-            uint32_t mbits = max(m & 0xFFFFu, m >> 16);
-            mbits = max(mbits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mbits), 1, kWave)));
+            uint32_t m = packed_max_u16(yp[0] & 0x7FFF7FFFu, yp[1] & 0x7FFF7FFFu);
+#pragma unroll
+            for (int q = 2; q < 8; ++q) m = packed_max_u16(m, yp[q] & 0x7FFF7FFFu);
+            const uint32_t mbits = max(m & 0xFFFFu, m >> 16);
             const float bmax = __uint_as_float(mbits << 16);
             const float tq = bmax * kRcp6;
             const float s = gs * tq;
-            const uint32_t sf = e4m3_satfinite(s);
-            const float sf_f = e4m3_value(sf);
+            const uint32_t sf = e4m3_scale_code(s);
+            const float sf_f = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sf), 0);
             const float d = sf_f * rcp_gs;
             const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
-            uint32_t word = 0;
+            uint32_t w0 = 0, w1 = 0;
             if (mbits < 0x7F80u && fabsf(outs) < INFINITY) {
                 // q = y * out with -0 turned into +0 (fma with a +0 addend, one
                 // rounding); the hardware E2M1 conversion with unit scale rounds
                 // finite values to nearest even and saturates.
-                word = fp4_pair<0>(word, yp[0], outs);
-                word = fp4_pair<1>(word, yp[1], outs);
-                word = fp4_pair<2>(word, yp[2], outs);
-                word = fp4_pair<3>(word, yp[3], outs);
+                w0 = fp4_pair<0>(w0, yp[0], outs);
+                w0 = fp4_pair<1>(w0, yp[1], outs);
+                w0 = fp4_pair<2>(w0, yp[2], outs);
+                w0 = fp4_pair<3>(w0, yp[3], outs);
+                w1 = fp4_pair<0>(w1, yp[4], outs);
+                w1 = fp4_pair<1>(w1, yp[5], outs);
+                w1 = fp4_pair<2>(w1, yp[6], outs);
+                w1 = fp4_pair<3>(w1, yp[7], outs);
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    word |= e2m1_code(bf16_lo(yp[q]) * outs) << (8 * q);
-                    word |= e2m1_code(bf16_hi(yp[q]) * outs) << (8 * q + 4);
+                    w0 |= e2m1_code(bf16_lo(yp[q]) * outs) << (8 * q);
+                    w0 |= e2m1_code(bf16_hi(yp[q]) * outs) << (8 * q + 4);
+                    w1 |= e2m1_code(bf16_lo(yp[q + 4]) * outs) << (8 * q);
+                    w1 |= e2m1_code(bf16_hi(yp[q + 4]) * outs) << (8 * q + 4);
                 }
             }
-            if (tok_ok && v < nvec) {
-                packed[static_cast<size_t>(t) * nvec + v] = word;
-                if ((v & 1) == 0) scales[static_cast<size_t>(t) * (nvec >> 1) + (v >> 1)] = static_cast<uint8_t>(sf);
+            if (tok_ok && b < nblk) {
+                packed[static_cast<size_t>(t) * nblk + b] = make_uint2(w0, w1);
+                scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf);
             }
         }
     }
 }
 
-template <int VPT>
+struct BlockGeom {
+    int tpt;   // threads per token (power of two, <= 256)
+    int bpt;   // 16-element blocks per thread
+};
+
+inline BlockGeom block_geom(int H) {
+    const int nblk = H / 16;
+    BlockGeom g;
+    g.tpt = 1;
+    while (g.tpt < nblk && g.tpt < kRowBlock) g.tpt <<= 1;
+    g.bpt = (nblk + g.tpt - 1) / g.tpt;
+    return g;
+}
+
+template <int BPT>
 int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
-                      const float* global_scale, int T, int H, int shard, const RowGeom& geo,
+                      const float* global_scale, int T, int H, int shard, const BlockGeom& geo,
                       uint8_t* packed, uint8_t* scales, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
-    const int cap = device_cu_count() * 8;
+    // as many blocks as fit on the GPU at once; each loops over its tokens
+    const int cap = device_cu_count() * resident_blocks(norm_quant_kernel<BPT>, kRowBlock, 0);
     const int grid = needed < cap ? needed : cap;
-    return launch(norm_quant_kernel<VPT>, dim3(grid), dim3(kRowBlock), 0, stream,
+    return launch(norm_quant_kernel<BPT>, dim3(grid), dim3(kRowBlock), 0, stream,
                   reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
-                  shard / 8, geo.tpt, reinterpret_cast<uint32_t*>(packed), scales);
+                  shard / 8, geo.tpt, reinterpret_cast<uint2*>(packed), scales);
 }
 
 }  // namespace
@@ -226,14 +232,12 @@ extern "C" int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, con
     if (T == 0) return MOE_OK;
     if (!x || !norm_w || !global_scale || !packed || !scales) return MOE_ERR_NULL_ARG;
     if (!all_aligned16(x, norm_w, packed, scales)) return MOE_ERR_ALIGN;
-    const RowGeom geo = row_geom(H);
-    int vpt = 1;
-    while (vpt < geo.vpt) vpt <<= 1;
-    switch (vpt) {
+    const BlockGeom geo = block_geom(H);
+    switch (geo.bpt) {
         case 1: return launch_norm_quant<1>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
         case 2: return launch_norm_quant<2>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
+        case 3: return launch_norm_quant<3>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
         case 4: return launch_norm_quant<4>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
-        case 8: return launch_norm_quant<8>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
         default: return MOE_ERR_BAD_SHAPE;
     }
 }

@@ -78,38 +78,42 @@ __device__ __forceinline__ int slot_bytes(int row, int c) { return (row * 2 + (c
 // Block 0 also clears the 256-byte zero block the projection reads in place
 // of out-of-range input.
 //
-// One thread per 16-byte output slot, in memory order (the writes stream);
-// each reads the 8 FP32 weights its slot holds a plane of.
+// One thread per fragment lane and K-step: it reads its 8 FP32 weights once
+// (32 bytes) and writes their three planes, so each wave writes three 1 KB
+// runs.
 __global__ __launch_bounds__(256) void split_weight_kernel(const float* __restrict__ W, int E, int H,
                                                            int G, int tiles_n,
                                                            u32x4* __restrict__ frags,
                                                            uint32_t* __restrict__ zero_block) {
     if (blockIdx.x == 0 && threadIdx.x < 64) zero_block[threadIdx.x] = 0u;
     const int nks = H / 16;
-    const int slots_per_step = 3 * G * 64;
-    const long long total = static_cast<long long>(tiles_n) * nks * slots_per_step;
+    const int per_step = G * 64;                       // (group, lane) pairs of one plane
+    const long long total = static_cast<long long>(tiles_n) * nks * per_step;
     const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
     for (long long s = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; s < total; s += stride) {
-        const long long blk = s / slots_per_step;         // tile * nks + K-step
-        const int sl = static_cast<int>(s - blk * slots_per_step);
+        const long long blk = s / per_step;            // tile * nks + K-step
+        const int sl = static_cast<int>(s - blk * per_step);
         const int tile = static_cast<int>(blk / nks);
         const int ks = static_cast<int>(blk - static_cast<long long>(tile) * nks);
-        const int frag = sl >> 6, l = sl & 63;
-        const int pl = frag / G, g = frag - pl * G;
+        const int g = sl >> 6, l = sl & 63;
         const int e = (tile * G + g) * 32 + (l & 31);
-        uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        uint32_t h[3][8];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) h[p][j] = 0u;
         if (e < E) {
             const float4* src = reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + ks * 16 + (l >> 5) * 8);
             const float4 a = src[0], b = src[1];
             const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint32_t p0, p1, p2;
-                split3(v[j], p0, p1, p2);
-                h[j] = pl == 0 ? p0 : (pl == 1 ? p1 : p2);
-            }
+            for (int j = 0; j < 8; ++j) split3(v[j], h[0][j], h[1][j], h[2][j]);
         }
-        frags[s] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        u32x4* out = frags + blk * (3 * per_step) + sl;
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            out[p * per_step] = u32x4{h[p][0] | (h[p][1] << 16), h[p][2] | (h[p][3] << 16),
+                                      h[p][4] | (h[p][5] << 16), h[p][6] | (h[p][7] << 16)};
     }
 }
 
@@ -364,7 +368,7 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
 
     const int cap = device_cu_count() * 8;
     const int G = 4 * p.nt;   // 32-expert groups per expert tile
-    const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * 3 * G * kWave;
+    const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * G * kWave;   // threads
     const int gw = ceil_div(wslots, 256);
     int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, G,
                     p.tiles_n, reinterpret_cast<u32x4*>(w_planes), reinterpret_cast<uint32_t*>(zero));
