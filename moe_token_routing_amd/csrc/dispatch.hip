@@ -18,6 +18,10 @@
 //             chunk are matched with ballots over the id bits, so the rank
 //             of a slot is the number of earlier slots with its id: the order
 //             within an expert is ascending slot index.
+// When the tile histograms are small (tiles^2 * E below kFuseLimit, every
+// shape up to tens of thousands of slots), step 2 is folded into step 3:
+// each place block sums the histograms itself -- its own exclusive prefix
+// over the tiles and every expert's total -- which saves a launch.
 #include <cmath>
 
 #include "launch.hpp"
@@ -28,6 +32,8 @@ namespace {
 constexpr int kDispBlock = 256;
 constexpr int kDispWaves = kDispBlock / kWave;
 constexpr int kMaxTiles = 256;
+constexpr long long kFuseLimit = 1ll << 22;   // tiles * tiles * E read by the fused place step
+constexpr int kHistBatch = 8;                 // tile histograms loaded before they are added
 
 struct TilePlan {
     int n;        // slots
@@ -103,10 +109,15 @@ __global__ __launch_bounds__(kDispBlock) void scan_kernel(int32_t* __restrict__ 
     }
 }
 
-// LDS layout: off[E + 1] then hist[kDispWaves][E].
+// LDS layout: off[E + 1], hist[kDispWaves][E], then (FUSED) cnt[E], rel[E].
+// FUSED: tile_hist holds the raw tile histograms; the block derives the
+// expert totals (block 0 writes them to counts) and its exclusive prefix
+// over the tiles. Otherwise tile_hist holds the prefixes and counts the
+// totals, from scan_kernel.
+template <bool FUSED>
 __global__ __launch_bounds__(kDispBlock) void place_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int tile,
-    const int32_t* __restrict__ tile_rel, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ ids, int n, int E, int tile, int tiles,
+    const int32_t* __restrict__ tile_hist, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ dest) {
     extern __shared__ int32_t lds[];
     int32_t* off = lds;
@@ -115,12 +126,39 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     const int tid = threadIdx.x;
     const int lane = __lane_id();
     const int wave = tid / kWave;
+    const int32_t* cnt = counts;
+    const int32_t* rel = tile_hist + static_cast<size_t>(blockIdx.x) * E;
+    if (FUSED) {
+        int32_t* cnt_l = hist + kDispWaves * E;
+        int32_t* rel_l = cnt_l + E;
+        for (int e = tid; e < E; e += kDispBlock) {
+            int before = 0, total = 0;
+#pragma unroll 1
+            for (int t0 = 0; t0 < tiles; t0 += kHistBatch) {
+                int v[kHistBatch];
+#pragma unroll
+                for (int u = 0; u < kHistBatch; ++u)
+                    v[u] = t0 + u < tiles ? tile_hist[static_cast<size_t>(t0 + u) * E + e] : 0;
+#pragma unroll
+                for (int u = 0; u < kHistBatch; ++u) {
+                    total += v[u];
+                    if (t0 + u < static_cast<int>(blockIdx.x)) before += v[u];
+                }
+            }
+            cnt_l[e] = total;
+            rel_l[e] = before;
+            if (blockIdx.x == 0) counts[e] = total;
+        }
+        __syncthreads();
+        cnt = cnt_l;
+        rel = rel_l;
+    }
 
     // (1) offsets = exclusive scan of counts: contiguous chunk per thread.
     const int chunk = (E + kDispBlock - 1) / kDispBlock;
     const int c0 = min(E, tid * chunk), c1 = min(E, c0 + chunk);
     int local = 0;
-    for (int e = c0; e < c1; ++e) local += counts[e];
+    for (int e = c0; e < c1; ++e) local += cnt[e];
     int incl = local;   // inclusive scan over the block, in thread order
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -135,7 +173,7 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     int run = before + incl - local;
     for (int e = c0; e < c1; ++e) {
         off[e] = run;
-        run += counts[e];
+        run += cnt[e];
     }
     if (tid == kDispBlock - 1) off[E] = before + incl;
     __syncthreads();
@@ -154,7 +192,6 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     }
     __syncthreads();
     // (3) starting position of each wave's run of each expert.
-    const int32_t* rel = tile_rel + static_cast<size_t>(blockIdx.x) * E;
     for (int e = tid; e < E; e += kDispBlock) {
         int p = off[e] + rel[e];
 #pragma unroll
@@ -234,11 +271,14 @@ extern "C" int moe_dispatch(const int32_t* topk_ids, int T, int k, int E, int32_
     int rc = launch(hist_kernel, dim3(p.tiles), dim3(kDispBlock), sizeof(int32_t) * E, stream,
                     topk_ids, p.n, E, p.tile, tile_counts);
     if (rc) return rc;
+    const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) + 1 + static_cast<size_t>(kDispWaves) * E);
+    if (static_cast<long long>(p.tiles) * p.tiles * E <= kFuseLimit)
+        return launch(place_kernel<true>, dim3(p.tiles), dim3(kDispBlock), lds + sizeof(int32_t) * 2 * E,
+                      stream, topk_ids, p.n, E, p.tile, p.tiles, static_cast<const int32_t*>(tile_counts),
+                      counts, offsets, perm, dest);
     rc = launch(scan_kernel, dim3(ceil_div(E, kWave)), dim3(kDispBlock), 0, stream, tile_counts,
                 p.tiles, E, counts);
     if (rc) return rc;
-    const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) + 1 + static_cast<size_t>(kDispWaves) * E);
-    return launch(place_kernel, dim3(p.tiles), dim3(kDispBlock), lds, stream, topk_ids, p.n, E,
-                  p.tile, static_cast<const int32_t*>(tile_counts),
-                  static_cast<const int32_t*>(counts), offsets, perm, dest);
+    return launch(place_kernel<false>, dim3(p.tiles), dim3(kDispBlock), lds, stream, topk_ids, p.n, E,
+                  p.tile, p.tiles, static_cast<const int32_t*>(tile_counts), counts, offsets, perm, dest);
 }

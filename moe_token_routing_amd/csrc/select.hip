@@ -45,15 +45,26 @@ __device__ __forceinline__ float sigmoid_rn(float l) {
     return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
 }
 
+constexpr int kSplitBatch = 8;   // split partials loaded before they are added
+
 // logit of (t, e): the split partial sums in order, times the scale (and
-// stored), or the caller's logit
+// stored), or the caller's logit. The partials of a batch are all loaded
+// before the first of them is added, so their latencies overlap; the sum
+// still runs over the splits in order.
 __device__ __forceinline__ float token_logit(const float* __restrict__ partials, int nsplit,
                                              size_t plane, float scale, int logits_in,
                                              float* __restrict__ logits, size_t idx) {
     if (logits_in) return logits[idx];
     float s = partials[idx];
 #pragma unroll 1
-    for (int p = 1; p < nsplit; ++p) s += partials[p * plane + idx];
+    for (int p0 = 1; p0 < nsplit; p0 += kSplitBatch) {
+        float q[kSplitBatch];
+#pragma unroll
+        for (int u = 0; u < kSplitBatch; ++u) q[u] = p0 + u < nsplit ? partials[(p0 + u) * plane + idx] : 0.f;
+#pragma unroll
+        for (int u = 0; u < kSplitBatch; ++u)
+            if (p0 + u < nsplit) s += q[u];
+    }
     const float l = s * scale;
     logits[idx] = l;
     return l;
@@ -121,12 +132,26 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
             load_run<EPL>(logits + row, vec, n, lg);
         } else {
             load_run<EPL>(partials + row, vec, n, lg);
+            // a batch of splits is loaded before any is added (the loads
+            // overlap); the sum still runs over the splits in order
 #pragma unroll 1
-            for (int p = 1; p < nsplit; ++p) {
-                float q[EPL];
-                load_run<EPL>(partials + p * plane + row, vec, n, q);
+            for (int p0 = 1; p0 < nsplit; p0 += kSplitBatch) {
+                float q[kSplitBatch][EPL];
 #pragma unroll
-                for (int i = 0; i < EPL; ++i) lg[i] += q[i];
+                for (int u = 0; u < kSplitBatch; ++u) {
+                    if (p0 + u < nsplit) {
+                        load_run<EPL>(partials + (p0 + u) * plane + row, vec, n, q[u]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < EPL; ++i) q[u][i] = 0.f;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kSplitBatch; ++u)
+                    if (p0 + u < nsplit) {
+#pragma unroll
+                        for (int i = 0; i < EPL; ++i) lg[i] += q[u][i];
+                    }
             }
 #pragma unroll
             for (int i = 0; i < EPL; ++i) {
