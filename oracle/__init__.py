@@ -26,5 +26,6 @@ from .nvfp4 import (gain_f32, rmsnorm_exact, rmsnorm_bf16, nvfp4_quantize,
                     norm_quant_nvfp4, global_scale, midpoint_boundary_blocks, dequantize,
                     rank_block_rows, norm_quant_nvfp4_rank_block)
 from .combine import combine
+from .fc1 import relu2, fc1_exact, expert_fc1_nvfp4, fc1_boundary_blocks
 
 __all__ = [n for n in dir() if not n.startswith("_")]
