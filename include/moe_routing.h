@@ -18,6 +18,11 @@
  *                         routing-weight scaling and top-k sum; invalid slots
  *                         are never read
  *
+ * and, beside the path, the expert FC1 the dispatch feeds:
+ *
+ *   moe_expert_fc1_nvfp4  gather grouped GEMM of the NVFP4 input with NVFP4
+ *                         per-expert weights, Relu2, NVFP4 output
+ *
  * Conventions shared by every call:
  *   - Every array argument is a DEVICE pointer (memory the caller allocated on
  *     the current HIP device), row-major, contiguous and 16-byte aligned
@@ -226,6 +231,53 @@ int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, const float* n
 int moe_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
                 const float* norm_w, float gain_center, float eps, int T, int H, int k,
                 uint16_t* out, void* stream);
+
+/*
+ * moe_expert_fc1_nvfp4 — the expert FC1 on the dispatched NVFP4 input: a
+ * gather grouped GEMM per expert, Relu2, NVFP4 output.
+ *
+ * Defined by TensorRT-LLM PR #21842 ("CuTe DSL act-fusion GEMMs: key the
+ * early accumulator release on the loop index"), description: the NVFP4 MoE
+ * FC1 is a block-scaled gather grouped GEMM with a fused activation (Relu2 on
+ * its K 1024, N 2688, 512-expert, top-22 workload) whose outputs are FP4
+ * values and their scale factors; the NVFP4 format and block quantiser are
+ * those of moe_norm_quant_nvfp4; the grouping is moe_dispatch's.
+ *
+ * For grouped position p < offsets[E], expert e with offsets[e] <= p <
+ * offsets[e+1], token t = perm[p] / k, and n < N:
+ *   v[p,n] = sum_i xv(t,i) * wv(e,n,i),  xv = code * scale / x_gs,
+ *                                         wv = code * scale / w_gs[e]
+ *   y[p,n] = max(v, 0)^2                  (FP32 accumulation)
+ * y is quantised per 16 consecutive n with the static scale y_gs exactly as
+ * moe_norm_quant_nvfp4 quantises its normalised rows. Positions p >=
+ * offsets[E] get zero codes and zero scales.
+ *
+ *   x_packed [T, K/2] u8, x_scales [T, K/16] u8 (E4M3): the NVFP4 input of
+ *            each token (moe_norm_quant_nvfp4's output); x_gs -> one FP32.
+ *   perm [T*k], offsets [E+1]: moe_dispatch's outputs for the same T, k, E.
+ *   w_packed [E, N, K/2] u8, w_scales [E, N, K/16] u8: per-expert weights
+ *            (output features x input features, NVFP4 along K);
+ *            w_gs [E] FP32 (device).
+ *   y_gs -> one FP32 (device): static output global scale.
+ *   y_packed [T*k, N/2] u8, y_scales [T*k, N/16] u8: outputs, rows in
+ *            grouped (perm) order.
+ *   T >= 0, 1 <= k <= MOE_MAX_TOPK, 1 <= E <= MOE_MAX_EXPERTS,
+ *   64 <= K <= MOE_MAX_HIDDEN with K % 64 == 0, N >= 128 with N % 128 == 0.
+ *   x_packed, w_packed, y_packed, y_scales, workspace 16-byte aligned;
+ *   x_scales, w_scales 4-byte aligned.
+ *   workspace: at least moe_expert_fc1_workspace_bytes(E) bytes.
+ * A perm entry outside [0, T*k) reads no input (its row is computed from
+ * zeros); NaN scale bytes (0x7F, 0xFF) in the inputs are not supported.
+ * Errors: NULL_ARG, BAD_SHAPE, ALIGN, WORKSPACE, HIP.
+ */
+size_t moe_expert_fc1_workspace_bytes(int E);
+
+int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_gs,
+                         const int32_t* perm, const int32_t* offsets, int T, int k,
+                         const uint8_t* w_packed, const uint8_t* w_scales, const float* w_gs,
+                         const float* y_gs, int K, int N, int E,
+                         uint8_t* y_packed, uint8_t* y_scales,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

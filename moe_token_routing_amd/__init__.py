@@ -42,6 +42,9 @@ _SIGNATURES = {
                                                  _vp, _vp, _vp]),
     "moe_combine": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_float, _c_float, _c_int, _c_int, _c_int,
                              _vp, _vp]),
+    "moe_expert_fc1_workspace_bytes": (_c_size, [_c_int]),
+    "moe_expert_fc1_nvfp4": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                      _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -256,3 +259,47 @@ def combine(expert_out: torch.Tensor, slots: torch.Tensor, topk_w: torch.Tensor,
         _ptr(expert_out), R, _ptr(slots), _ptr(topk_w), _ptr(norm_w), float(gain_center), float(eps),
         T, H, k, _ptr(out), _stream(dev)))
     return out
+
+
+def expert_fc1_workspace_bytes(E: int) -> int:
+    return int(lib().moe_expert_fc1_workspace_bytes(E))
+
+
+def expert_fc1_nvfp4(x_packed: torch.Tensor, x_scales: torch.Tensor, x_gs: torch.Tensor,
+                     perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                     w_packed: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
+                     y_gs: torch.Tensor, *, y_packed=None, y_scales=None, workspace=None):
+    """moe_expert_fc1_nvfp4. x_packed [T,K/2] / x_scales [T,K/16] uint8 (the
+    NVFP4 input), perm [T*k] / offsets [E+1] int32 (moe_dispatch's grouping),
+    w_packed [E,N,K/2] / w_scales [E,N,K/16] uint8, w_gs [E] fp32, x_gs and
+    y_gs one-element fp32 GPU tensors. Returns (y_packed [T*k,N/2],
+    y_scales [T*k,N/16]) uint8 in grouped order."""
+    dev = x_packed.device
+    if x_packed.dim() != 2 or w_packed.dim() != 3:
+        raise ValueError("x_packed must be [T,K/2] and w_packed [E,N,K/2]")
+    T, K = x_packed.shape[0], x_packed.shape[1] * 2
+    E, N = w_packed.shape[0], w_packed.shape[1]
+    _need(x_packed, "x_packed", (torch.uint8,), (T, K // 2), dev)
+    _need(x_scales, "x_scales", (torch.uint8,), (T, K // 16), dev)
+    _need(w_packed, "w_packed", (torch.uint8,), (E, N, K // 2), dev)
+    _need(w_scales, "w_scales", (torch.uint8,), (E, N, K // 16), dev)
+    _need(w_gs, "w_gs", (torch.float32,), (E,), dev)
+    _need(perm, "perm", (torch.int32,), (T * k,), dev)
+    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    for name, g in (("x_gs", x_gs), ("y_gs", y_gs)):
+        _need(g, name, (torch.float32,), None, dev)
+        if g.numel() != 1:
+            raise ValueError(name + " must hold one value")
+    P = T * k
+    y_packed = torch.empty((P, N // 2), dtype=torch.uint8, device=dev) if y_packed is None else y_packed
+    y_scales = torch.empty((P, N // 16), dtype=torch.uint8, device=dev) if y_scales is None else y_scales
+    _need(y_packed, "y_packed", (torch.uint8,), (P, N // 2), dev)
+    _need(y_scales, "y_scales", (torch.uint8,), (P, N // 16), dev)
+    need = expert_fc1_workspace_bytes(E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("moe_expert_fc1_nvfp4", lib().moe_expert_fc1_nvfp4(
+        _ptr(x_packed), _ptr(x_scales), _ptr(x_gs), _ptr(perm), _ptr(offsets), T, int(k),
+        _ptr(w_packed), _ptr(w_scales), _ptr(w_gs), _ptr(y_gs), K, N, E,
+        _ptr(y_packed), _ptr(y_scales), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return y_packed, y_scales

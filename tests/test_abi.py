@@ -29,7 +29,8 @@ def test_every_declared_function_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"moe_status_string", "moe_route_workspace_bytes", "moe_route",
                           "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_norm_quant_nvfp4",
-                          "moe_norm_quant_nvfp4_rank_block", "moe_combine"}
+                          "moe_norm_quant_nvfp4_rank_block", "moe_combine",
+                          "moe_expert_fc1_workspace_bytes", "moe_expert_fc1_nvfp4"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(m._SIGNATURES)
@@ -120,3 +121,20 @@ def test_dispatch_rejects_before_launch(lib):
     assert f(FAKE, 4, 2, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     assert f(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -4
     assert f(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -4
+
+
+def test_expert_fc1_rejects_before_launch(lib):
+    f = lib.moe_expert_fc1_nvfp4
+    ws = lib.moe_expert_fc1_workspace_bytes(8)
+    assert ws >= 9 * 4 and ws % 256 == 0
+    assert lib.moe_expert_fc1_workspace_bytes(0) == 0
+    args = lambda T=4, k=2, K=128, N=256, E=8, ws_b=ws, x=FAKE: (
+        x, FAKE, FAKE, FAKE, FAKE, T, k, FAKE, FAKE, FAKE, FAKE, K, N, E, FAKE, FAKE, FAKE, ws_b, None)
+    assert f(*args(K=96)) == -2        # K % 64
+    assert f(*args(N=200)) == -2       # N % 128
+    assert f(*args(E=0)) == -2
+    assert f(*args(k=33)) == -2
+    assert f(*args(T=-1)) == -2
+    assert f(*args(x=None)) == -1
+    assert f(*args(ws_b=ws - 1)) == -4
+    assert f(*args(T=0)) == 0

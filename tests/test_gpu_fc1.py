@@ -1,0 +1,137 @@
+"""moe_expert_fc1_nvfp4 against the oracle: codes and scales bit-exact
+outside the boundary set (blocks an FP32 accumulation may legitimately
+change), within one step inside it; zero rows past the routed count; empty
+and many-tile experts; the FC1 workload the act-fusion GEMM page times
+(K 1024, N 2688, 512 experts, top-22) at full size, sampled."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as wl
+from gpu_helpers import dev, e2m1_step_distance, host, note, require_gpu, scalar_dev, unpack_codes
+
+pytestmark = pytest.mark.gpu
+
+m = pytest.importorskip("moe_token_routing_amd")
+
+
+def _routing(g, T, k, E, invalid=0.0, skew=None):
+    ids = np.empty((T, k), dtype=np.int32)
+    p = None
+    if skew is not None:
+        p = np.asarray(skew, dtype=np.float64)
+        p = p / p.sum()
+    for t in range(T):
+        ids[t] = g.choice(E, size=k, replace=False, p=p)
+    if invalid:
+        ids[g.uniform(size=(T, k)) < invalid] = -1
+    counts, offsets, perm, dest = O.dispatch(ids, E)
+    return perm.astype(np.int32), offsets.astype(np.int32)
+
+
+def _run(xp, xs, gx, perm, offsets, k, wp, ws, gw, gy, what):
+    require_gpu()
+    note("fc1 %s T=%d K=%d N=%d E=%d k=%d" % (what, xp.shape[0], xp.shape[1] * 2, wp.shape[1], wp.shape[0], k))
+    yp, ys = m.expert_fc1_nvfp4(dev(xp), dev(xs), scalar_dev(gx), dev(perm), dev(offsets), k,
+                                dev(wp), dev(ws), dev(gw), scalar_dev(gy))
+    torch.cuda.synchronize()
+    return host(yp), host(ys)
+
+
+def _check(got_p, got_s, ref_p, ref_s, near, what):
+    gc, rc = unpack_codes(got_p), unpack_codes(ref_p)
+    nearel = np.repeat(near, 16, axis=1)
+    assert np.array_equal(got_s[~near], ref_s[~near]), what + ": scale mismatch outside the boundary set"
+    bad = (gc != rc) & ~nearel
+    assert not bad.any(), "%s: %d code mismatches outside the boundary set" % (what, int(bad.sum()))
+    if near.any():
+        assert (np.abs(got_s[near].astype(int) - ref_s[near].astype(int)) <= 1).all()
+        assert (e2m1_step_distance(gc[nearel], rc[nearel]) <= 1).all()
+    return int(near.sum()), int(((gc != rc) & nearel).sum())
+
+
+def _case(T, k, E, K, N, seed, invalid=0.0, skew=None):
+    g = np.random.default_rng(seed)
+    w = wl.WORKLOADS["wide_k"]
+    xp, xs = wl.fc1_activations(w, T, K)
+    wp, ws, gw = wl.fc1_weights(w, N, E, K)
+    perm, offsets = _routing(g, T, k, E, invalid, skew)
+    gx = np.float32(37.5)
+    acc, _ = O.fc1_exact(xp, xs, gx, perm, offsets, k, wp, ws, gw)
+    gy = O.global_scale(O.relu2(acc))
+    return xp, xs, gx, perm, offsets, k, wp, ws, gw, gy
+
+
+@pytest.mark.parametrize("T,k,E,K,N,invalid,skew", [
+    (37, 3, 5, 128, 256, 0.1, None),            # ragged tiles, invalid slots
+    (300, 2, 4, 64, 128, 0.0, [10, 0, 1, 3]),   # an empty expert, one expert over several tiles
+    (64, 4, 16, 256, 384, 0.0, None),           # many small experts
+])
+def test_fc1_small(T, k, E, K, N, invalid, skew):
+    args = _case(T, k, E, K, N, seed=T + E, invalid=invalid, skew=skew)
+    xp, xs, gx, perm, offsets, k, wp, ws, gw, gy = args
+    got_p, got_s = _run(*args, "small")
+    ref_p, ref_s = O.expert_fc1_nvfp4(*args)
+    near = O.fc1_boundary_blocks(*args)
+    nset, nmis = _check(got_p, got_s, ref_p, ref_s, near, "fc1")
+    used = int(offsets[-1])
+    assert not got_p[used:].any() and not got_s[used:].any()
+    print("boundary blocks %d of %d, code mismatches inside %d" % (nset, near.size, nmis))
+
+
+def test_fc1_deterministic():
+    args = _case(100, 3, 6, 128, 256, seed=4)
+    a = _run(*args, "determinism 1")
+    b = _run(*args, "determinism 2")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_fc1_zero_tokens():
+    require_gpu()
+    E, K, N = 4, 64, 128
+    yp, ys = m.expert_fc1_nvfp4(torch.zeros((0, K // 2), dtype=torch.uint8, device="cuda"),
+                                torch.zeros((0, K // 16), dtype=torch.uint8, device="cuda"),
+                                scalar_dev(1.0), torch.zeros(0, dtype=torch.int32, device="cuda"),
+                                torch.zeros(E + 1, dtype=torch.int32, device="cuda"), 2,
+                                torch.zeros((E, N, K // 2), dtype=torch.uint8, device="cuda"),
+                                torch.zeros((E, N, K // 16), dtype=torch.uint8, device="cuda"),
+                                torch.ones(E, dtype=torch.float32, device="cuda"), scalar_dev(1.0))
+    assert yp.shape == (0, N // 2) and ys.shape == (0, N // 16)
+
+
+def test_fc1_full_workload_sampled():
+    """T = 32768 tokens, top-22 of 512 experts, K 1024, N 2688, at full size;
+    rows of 6 experts checked against the oracle."""
+    require_gpu()
+    w = wl.WORKLOADS["wide_k"]
+    T, k, E, K, N = w.T, w.k, w.E, w.H, wl.FC1_N["wide_k"]
+    xp, xs = wl.fc1_activations(w, T, K)
+    wp, ws, gw = wl.fc1_weights(w, N, E, K)
+    ids = wl.synthetic_topk_ids(w, T)
+    counts, offsets, perm, dest = O.dispatch(ids, E)
+    perm, offsets = perm.astype(np.int32), offsets.astype(np.int32)
+    gx = np.float32(37.5)
+    g = np.random.default_rng(11)
+    experts = g.choice(E, size=6, replace=False)
+    rows = np.concatenate([np.arange(offsets[e], offsets[e + 1])[:24] for e in experts])
+    # the sampled rows as a problem of their own: same tokens and experts
+    sub_ids = np.full((len(rows), 1), -1, dtype=np.int32)
+    sub_exp = np.array([np.searchsorted(offsets, r, side="right") - 1 for r in rows])
+    sub_ids[:, 0] = sub_exp
+    c2, off2, perm2, _ = O.dispatch(sub_ids, E)
+    tok = perm[rows] // k
+    sx_p, sx_s = xp[tok], xs[tok]
+    sub_args = (sx_p, sx_s, gx, perm2.astype(np.int32), off2.astype(np.int32), 1, wp, ws, gw)
+    acc, _ = O.fc1_exact(*sub_args)
+    gy = O.global_scale(O.relu2(acc))
+    ref_p, ref_s = O.expert_fc1_nvfp4(*sub_args, gy)
+    near = O.fc1_boundary_blocks(*sub_args, gy)
+    got_p, got_s = _run(xp, xs, gx, perm, offsets, k, wp, ws, gw, gy, "wide_k full")
+    # sub-problem position q holds sampled row rows[perm2[q]]
+    got_rows_p = got_p[rows[perm2]]
+    got_rows_s = got_s[rows[perm2]]
+    nset, nmis = _check(got_rows_p, got_rows_s, ref_p, ref_s, near, "fc1 wide_k")
+    used = int(offsets[-1])
+    assert used == T * k
+    print("wide_k sampled rows %d: boundary blocks %d of %d, mismatches inside %d" % (len(rows), nset, near.size, nmis))

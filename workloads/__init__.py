@@ -85,7 +85,11 @@ WORKLOADS = {
 
 # Field order fixes the child stream each field draws from.
 _FIELDS = ["hidden", "W", "bias", "mask", "tie_logits", "expert_out", "slots",
-           "combine_gain", "quant_x", "quant_gain", "topk_w"]
+           "combine_gain", "quant_x", "quant_gain", "topk_w", "fc1_x", "fc1_w"]
+
+# Output features of the expert FC1 where a workload stands for the FC1 the
+# act-fusion GEMM page times (K 1024, N 2688, 512 experts, top-22).
+FC1_N = {"wide_k": 2688}
 
 
 def rng(workload: Workload, field: str) -> np.random.Generator:
@@ -270,3 +274,35 @@ def quant_gain(w: Workload) -> np.ndarray:
     gain_center + weight."""
     g = rng(w, "quant_gain")
     return ((g.uniform(size=w.H) * 2.0 - 1.0) * w.quant_gain_lim).astype(np.float32)
+
+
+# E4M3 scale bytes drawn for NVFP4 inputs: exponent fields 6..8, i.e.
+# magnitudes 0.5 .. 1.875 * 2 (any byte below 0x7F is a valid scale).
+_FC1_SCALE_LO, _FC1_SCALE_HI = 0x30, 0x48
+
+
+def fc1_activations(w: Workload, T: Optional[int] = None, K: Optional[int] = None):
+    """NVFP4 input of the expert FC1 drawn as raw bytes: packed [T, K/2]
+    (two uniform E2M1 codes per byte, signs included) and scales [T, K/16]
+    (E4M3 bytes); K defaults to the workload's hidden size."""
+    T = w.T if T is None else T
+    K = w.H if K is None else K
+    g = rng(w, "fc1_x")
+    packed = g.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
+    scales = g.integers(_FC1_SCALE_LO, _FC1_SCALE_HI, size=(T, K // 16), dtype=np.uint8)
+    return packed, scales
+
+
+def fc1_weights(w: Workload, N: int, E: Optional[int] = None, K: Optional[int] = None):
+    """NVFP4 FC1 weights drawn as raw bytes: packed [E, N, K/2], scales
+    [E, N, K/16] (E4M3 bytes) and one FP32 global scale per expert in
+    U(1, 4)."""
+    E = w.E if E is None else E
+    K = w.H if K is None else K
+    g = rng(w, "fc1_w")
+    packed = np.empty((E, N, K // 2), dtype=np.uint8)
+    for e in range(E):   # per expert, to bound the temporary
+        packed[e] = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = g.integers(_FC1_SCALE_LO, _FC1_SCALE_HI, size=(E, N, K // 16), dtype=np.uint8)
+    gs = g.uniform(1.0, 4.0, size=E).astype(np.float32)
+    return packed, scales, gs
