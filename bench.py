@@ -32,6 +32,8 @@ Alongside the throughput the line carries:
                 is the HBM bytes per launch from the committed rocprofv3
                 counter summary, when that was taken on the current kernel
                 source (null otherwise)
+  expert_fc1    the expert FC1 (moe_expert_fc1_nvfp4) at the FC1 workload of
+                the act-fusion GEMM page, against the FP16 MFMA peak
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -49,6 +51,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense FP16 / BF16 matrix peak
 METRIC = "routed tokens/sec and % of HBM peak, H=8192 E=256 k=8, 8192 tokens"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_prefill_traffic.json")
 COMBINE_SRC = os.path.join(ROOT, "moe_token_routing_amd", "csrc", "combine.hip")
@@ -112,6 +115,46 @@ def cpu_baseline(w, sample_tokens: int):
             "sample": "first %d tokens of the %s workload as one batch, all four steps, %.1f s" % (S, w.name, dt)}
 
 
+def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10):
+    """The expert FC1 on the dispatched NVFP4 input at the FC1 workload the
+    act-fusion GEMM page times (K 1024, N 2688, 512 experts, top-22, 32768
+    tokens): synthetic NVFP4 bytes, the path's own dispatch of synthetic
+    top-22 ids, HIP events around each call."""
+    w = wl.WORKLOADS["wide_k"]
+    T, k, E, K, N = w.T, w.k, w.E, w.H, wl.FC1_N["wide_k"]
+    xp, xs = wl.fc1_activations(w, T, K)
+    wp, ws, gw = wl.fc1_weights(w, N, E, K)
+    ids = torch.from_numpy(wl.synthetic_topk_ids(w, T)).to(dev)
+    X, XS = torch.from_numpy(xp).to(dev), torch.from_numpy(xs).to(dev)
+    Wp, Ws, GW = torch.from_numpy(wp).to(dev), torch.from_numpy(ws).to(dev), torch.from_numpy(gw).to(dev)
+    del xp, xs, wp, ws
+    counts, offsets, perm, dest = m.dispatch(ids, E)
+    gx = torch.tensor([37.5], dtype=torch.float32, device=dev)
+    gy = torch.tensor([1.0e4], dtype=torch.float32, device=dev)
+    yp = torch.empty((T * k, N // 2), dtype=torch.uint8, device=dev)
+    ys = torch.empty((T * k, N // 16), dtype=torch.uint8, device=dev)
+    wsp = torch.empty(m.expert_fc1_workspace_bytes(E), dtype=torch.uint8, device=dev)
+
+    def call():
+        m.expert_fc1_nvfp4(X, XS, gx, perm, offsets, k, Wp, Ws, GW, gy, y_packed=yp, y_scales=ys, workspace=wsp)
+
+    for _ in range(2):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flop = 2.0 * T * k * N * K
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"workload": "K 1024, N 2688, 512 experts, top-22, 32768 tokens (720896 routed rows)",
+            "ms": round(ms, 3), "TFLOPs": round(tf, 1), "unit_peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
+            "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "bytes_in": int(T * K * 9 // 16 + E * N * K * 9 // 16), "bytes_out": int(T * k * N * 9 // 16)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +171,8 @@ def main():
                          "(overlap) or beside the route (overlap-route), or all on one stream (serial)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline schedule from a HIP graph instead of launching it eagerly")
+    ap.add_argument("--no-fc1", dest="fc1", action="store_false",
+                    help="skip timing the expert FC1 (K 1024, N 2688, 512 experts, top-22)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="serial steps timed after flushing the last-level cache (0: skip)")
     args = ap.parse_args()
@@ -319,6 +364,10 @@ def main():
         rank_block = {"tp": tp, "ms": round(rb_ms, 4), "same_bytes_as_contiguous": same}
         del pooled, rb_packed, rb_scales
 
+    fc1 = None
+    if args.fc1:
+        fc1 = time_expert_fc1(m, wl, torch, dev, stream)
+
     names = ["route", "dispatch", "norm_quant", "combine"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
@@ -375,6 +424,7 @@ def main():
         "hbm_frac_of_peak": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "valid_tokens_per_s": round(int(mask_np.sum()) / (ms_per_step * 1e-3), 1),
         "stages": stages,
+        "expert_fc1": fc1,
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
                       "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),
