@@ -133,7 +133,7 @@ def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10):
     gy = torch.tensor([1.0e4], dtype=torch.float32, device=dev)
     yp = torch.empty((T * k, N // 2), dtype=torch.uint8, device=dev)
     ys = torch.empty((T * k, N // 16), dtype=torch.uint8, device=dev)
-    wsp = torch.empty(m.expert_fc1_workspace_bytes(E), dtype=torch.uint8, device=dev)
+    wsp = torch.empty(m.expert_fc1_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
 
     def call():
         m.expert_fc1_nvfp4(X, XS, gx, perm, offsets, k, Wp, Ws, GW, gy, y_packed=yp, y_scales=ys, workspace=wsp)

@@ -265,12 +265,14 @@ int moe_combine(const uint16_t* expert_out, int R, const int32_t* slots, const f
  *   64 <= K <= MOE_MAX_HIDDEN with K % 64 == 0, N >= 128 with N % 128 == 0.
  *   x_packed, w_packed, y_packed, y_scales, workspace 16-byte aligned;
  *   x_scales, w_scales 4-byte aligned.
- *   workspace: at least moe_expert_fc1_workspace_bytes(E) bytes.
+ *   workspace: at least moe_expert_fc1_workspace_bytes(T, k, E) bytes
+ *            (per-expert tile starts and one 16-byte record per row tile of
+ *            256 grouped rows; 0 means T, k or E is out of range).
  * A perm entry outside [0, T*k) reads no input (its row is computed from
  * zeros); NaN scale bytes (0x7F, 0xFF) in the inputs are not supported.
  * Errors: NULL_ARG, BAD_SHAPE, ALIGN, WORKSPACE, HIP.
  */
-size_t moe_expert_fc1_workspace_bytes(int E);
+size_t moe_expert_fc1_workspace_bytes(int T, int k, int E);
 
 int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_gs,
                          const int32_t* perm, const int32_t* offsets, int T, int k,

@@ -42,7 +42,7 @@ _SIGNATURES = {
                                                  _vp, _vp, _vp]),
     "moe_combine": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_float, _c_float, _c_int, _c_int, _c_int,
                              _vp, _vp]),
-    "moe_expert_fc1_workspace_bytes": (_c_size, [_c_int]),
+    "moe_expert_fc1_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_expert_fc1_nvfp4": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp,
                                       _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
 }
@@ -261,8 +261,8 @@ def combine(expert_out: torch.Tensor, slots: torch.Tensor, topk_w: torch.Tensor,
     return out
 
 
-def expert_fc1_workspace_bytes(E: int) -> int:
-    return int(lib().moe_expert_fc1_workspace_bytes(E))
+def expert_fc1_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(lib().moe_expert_fc1_workspace_bytes(T, k, E))
 
 
 def expert_fc1_nvfp4(x_packed: torch.Tensor, x_scales: torch.Tensor, x_gs: torch.Tensor,
@@ -295,7 +295,7 @@ def expert_fc1_nvfp4(x_packed: torch.Tensor, x_scales: torch.Tensor, x_gs: torch
     y_scales = torch.empty((P, N // 16), dtype=torch.uint8, device=dev) if y_scales is None else y_scales
     _need(y_packed, "y_packed", (torch.uint8,), (P, N // 2), dev)
     _need(y_scales, "y_scales", (torch.uint8,), (P, N // 16), dev)
-    need = expert_fc1_workspace_bytes(E)
+    need = expert_fc1_workspace_bytes(T, int(k), E)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check("moe_expert_fc1_nvfp4", lib().moe_expert_fc1_nvfp4(

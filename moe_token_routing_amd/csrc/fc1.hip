@@ -26,9 +26,11 @@
 //    then dequantised into the other half of a double-buffered LDS tile
 //    (rows of 128 bytes, 16-byte chunks XOR-swizzled by row pair, so neither
 //    the stores nor the fragment reads conflict on LDS banks).
-//  * The tiles of each expert are found from `offsets` by a one-block kernel
-//    (exclusive prefix of ceil(rows / 128) over experts); the GEMM grid is an
-//    upper bound, blocks past the last tile leave at once. Blocks are
+//  * The row tiles of each expert are laid out from `offsets` by a one-block
+//    kernel (exclusive prefix of ceil(rows / 256) over experts, and one
+//    16-byte record per tile: expert, first row, row end), so a GEMM block
+//    learns its tile from one load; the grid is an upper bound, blocks past
+//    the last tile leave at once. Blocks are
 //    remapped so that each XCD walks a contiguous run of (column tile,
 //    expert, row tile), keeping an expert's weight slice in its L2.
 //  * Epilogue: alpha * acc, Relu2, staged in LDS as FP32 half a tile at a
@@ -45,31 +47,49 @@ namespace {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kFcBM = 256;              // grouped rows per block tile
 constexpr int kFcKS = 64;               // K per stage
-constexpr int kFcBlock = 512;           // eight waves
+constexpr int kFcTilesBlock = 512;      // threads of the tile-layout kernel
+constexpr int kFcRaw = 2;               // stages of raw bytes in registers
+constexpr int kFcSch = 8;               // stages per scale chunk: 4 scale bytes a stage, 32 a row
 
-// Block tile kFcBM x BN, eight waves in a WM x WN grid, each 32 MT x 32 NT.
+// Block tile BM x BN, WM x WN waves, each 32 MT x 32 NT; two threads per
+// A row (each loads half of a stage's 64 K), and the B rows' halves spread
+// over the threads NBI at a time.
 template <int WM, int WN, int MT, int NT>
 struct FcShape {
-    static_assert(WM * WN * kWave == kFcBlock && WM * MT * 32 == kFcBM, "tile");
+    static constexpr int BM = WM * MT * 32;
     static constexpr int BN = WN * NT * 32;
-    static constexpr int STAGE = (kFcBM + BN) * kFcKS * 2;          // A and B tiles, BF16 bytes
+    static constexpr int THREADS = WM * WN * kWave;
+    static_assert(THREADS == 2 * BM, "two threads per A row");
+    static constexpr int NBI = (2 * BN + THREADS - 1) / THREADS;      // B row halves per thread
+    static constexpr int STAGE = (BM + BN) * kFcKS * 2;              // A and B tiles, FP16 bytes
+    static constexpr int SCHUNK = (BM + BN) * kFcSch * 4;             // one scale chunk of every row
+    static constexpr size_t MAIN = 2 * static_cast<size_t>(STAGE) + 2 * static_cast<size_t>(SCHUNK);
     static constexpr int YSTRIDE = BN + 4;                            // floats per staged output row
-    static constexpr size_t YBYTES = static_cast<size_t>(kFcBM / 2) * YSTRIDE * 4;   // half the rows
-    static constexpr size_t LDS = 2 * static_cast<size_t>(STAGE) > YBYTES ? 2 * static_cast<size_t>(STAGE) : YBYTES;
+    static constexpr size_t YBYTES = static_cast<size_t>(BM / 2) * YSTRIDE * 4;   // half the rows
+    static constexpr size_t LDS = MAIN > YBYTES ? MAIN : YBYTES;
 };
 
-// tile_start[e] = sum over e' < e of ceil(rows(e') / kFcBM); tile_start[E] = total.
-__global__ __launch_bounds__(kFcBlock) void fc1_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                             int32_t* __restrict__ tile_start) {
-    __shared__ int32_t wsum[kFcBlock / kWave];
+// Row tiles of `bm` rows over experts: at most ceil(P / bm) + E (each
+// expert adds at most one partial tile).
+inline long long fc1_row_tiles_upper(long long P, int E, int bm) { return (P + bm - 1) / bm + E; }
+
+// tile_start[e] = sum over e' < e of ceil(rows(e') / bm); tile_start[E] =
+// total. Row tile t of expert e (tile_start[e] <= t < tile_start[e + 1]) is
+// described by tile_info[t] = (e, first grouped row, end of the expert's
+// rows clamped to n_pos, 0), so a GEMM block finds its tile with one load.
+__global__ __launch_bounds__(kFcTilesBlock) void fc1_tiles_kernel(const int32_t* __restrict__ offsets, int E,
+                                                                  int n_pos, int bm, int m_upper,
+                                                                  int32_t* __restrict__ tile_start,
+                                                                  int4* __restrict__ tile_info) {
+    __shared__ int32_t wsum[kFcTilesBlock / kWave];
     const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-    const int chunk = (E + kFcBlock - 1) / kFcBlock;
+    const int chunk = (E + kFcTilesBlock - 1) / kFcTilesBlock;
     const int e0 = min(E, tid * chunk), e1 = min(E, e0 + chunk);
     int local = 0;
-    for (int e = e0; e < e1; ++e) local += (max(offsets[e + 1] - offsets[e], 0) + kFcBM - 1) / kFcBM;
+    for (int e = e0; e < e1; ++e) local += (max(offsets[e + 1] - offsets[e], 0) + bm - 1) / bm;
     int incl = local;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -82,9 +102,14 @@ __global__ __launch_bounds__(kFcBlock) void fc1_tiles_kernel(const int32_t* __re
     for (int w = 0; w < wave; ++w) run += wsum[w];
     for (int e = e0; e < e1; ++e) {
         tile_start[e] = run;
-        run += (max(offsets[e + 1] - offsets[e], 0) + kFcBM - 1) / kFcBM;
+        const int first = offsets[e], end = offsets[e + 1];
+        const int n = (max(end - first, 0) + bm - 1) / bm;
+        // (valid offsets never make more than m_upper tiles; others stop there)
+        for (int i = 0; i < n && run + i < m_upper; ++i)
+            tile_info[run + i] = make_int4(e, first + i * bm, min(end, n_pos), 0);
+        run += n;
     }
-    if (tid == kFcBlock - 1) tile_start[E] = run;
+    if (tid == kFcTilesBlock - 1) tile_start[E] = run;
 }
 
 // Grouped positions past offsets[E] get zero codes and zero scales.
@@ -117,6 +142,27 @@ __device__ __forceinline__ void dequant8(uint32_t w, f16x2_t s2, uint32_t (&out)
     out[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
 }
 
+// Block barrier that orders LDS accesses only: the wave waits for its own LDS
+// operations (lgkmcnt 0), not for its global loads, which stay in flight
+// across the barrier (__syncthreads' release fence would wait for them too,
+// and the raw bytes of later stages are loaded exactly so that they can).
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Two E4M3 scale bytes (the low 16 bits) -> an FP16 pair: the packed FP8
+// decode is exact, and every E4M3 value is exact in FP16, so the
+// round-toward-zero packing does not round.
+__device__ __forceinline__ f16x2_t scale_pair(uint32_t two) {
+    const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(two), false);
+    return __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
+}
+
 // Row `row` of a stage tile is 128 bytes, eight 16-byte chunks; chunk c sits
 // at c ^ ((row >> 1) & 7): the MFMA fragment reads (16 consecutive rows, one
 // chunk) and the dequantised stores (8 rows x 2 chunks) then touch 16
@@ -124,80 +170,127 @@ __device__ __forceinline__ void dequant8(uint32_t w, f16x2_t s2, uint32_t (&out)
 __device__ __forceinline__ int chunk_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 template <int WM, int WN, int MT, int NT>
-__global__ __launch_bounds__(kFcBlock) __attribute__((amdgpu_waves_per_eu(2))) void fc1_gemm_kernel(
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void fc1_gemm_kernel(
     const uint8_t* __restrict__ x_packed, const uint8_t* __restrict__ x_scales,
-    const float* __restrict__ x_gs, const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_start, int k, const uint8_t* __restrict__ w_packed,
+    const float* __restrict__ x_gs, const int32_t* __restrict__ perm, const int32_t* __restrict__ tile_start,
+    const int4* __restrict__ tile_info, int k, const uint8_t* __restrict__ w_packed,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs, const float* __restrict__ y_gs,
     int K, int N, int E, int n_pos, int m_upper, int per_xcd, uint8_t* __restrict__ y_packed,
     uint8_t* __restrict__ y_scales) {
     using S = FcShape<WM, WN, MT, NT>;
-    constexpr int BN = S::BN;
+    constexpr int BM = S::BM, BN = S::BN, NBI = S::NBI;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
     // XCD-contiguous logical tile index: (column tile, row tile over experts)
     const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const int nt = logical / m_upper;
-    const int mt = logical - nt * m_upper;
-    if (nt >= N / BN || mt >= tile_start[E]) return;
-    // expert owning row tile mt: the last e with tile_start[e] <= mt
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int row_end = min(offsets[e + 1], n_pos);
-    const int m0 = offsets[e] + (mt - tile_start[e]) * kFcBM;
+    const int mt = logical - nt * m_upper;   // < m_upper: tile_info[mt] is in bounds
+    const int total = tile_start[E];
+    const int4 info = tile_info[mt];
+    if (nt >= N / BN || mt >= total) return;
+    const int e = info.x, m0 = info.y, row_end = info.z;
     const int n0 = nt * BN;
 
-    // this thread's load assignment: row r of the A tile (and of the B tile
-    // when r < BN), K half h of a stage
+    // this thread's load assignment: row r of the A tile, K half h of a
+    // stage; B row halves tid + i THREADS (i < NBI) of the 2 BN
     const int r = tid >> 1, h = tid & 1;
-    const bool b_row = r < BN;
     const int p = m0 + r;
     const int slot = p >= 0 && p < row_end ? perm[p] : -1;
     const bool a_ok = slot >= 0 && slot < n_pos;   // a slot outside [0, T k) reads nothing
     const int token = a_ok ? slot / k : 0;
     const size_t kb = static_cast<size_t>(K) / 2, ks = static_cast<size_t>(K) / 16;
     const uint8_t* xa = x_packed + static_cast<size_t>(token) * kb + h * 16;
-    const uint8_t* xsa = x_scales + static_cast<size_t>(token) * ks + h * 2;
-    const size_t wrow = static_cast<size_t>(e) * N + n0 + (b_row ? r : 0);
-    const uint8_t* wb = w_packed + wrow * kb + h * 16;
-    const uint8_t* wsb = w_scales + wrow * ks + h * 2;
+    const uint8_t* xsrow = x_scales + static_cast<size_t>(token) * ks;
+    bool b_ok[NBI];
+    int b_r[NBI], b_h[NBI];
+    const uint8_t* wb[NBI];
+    const uint8_t* wsb[NBI];
+#pragma unroll
+    for (int i = 0; i < NBI; ++i) {
+        const int idx = tid + i * S::THREADS;
+        b_ok[i] = idx < 2 * BN;
+        b_r[i] = b_ok[i] ? idx >> 1 : 0;
+        b_h[i] = idx & 1;
+        const size_t wrow = static_cast<size_t>(e) * N + n0 + b_r[i];
+        wb[i] = w_packed + wrow * kb + b_h[i] * 16;
+        wsb[i] = w_scales + wrow * ks;
+    }
 
-    // Raw FP4 bytes and scale bytes of one stage. Loads always read a valid
-    // row (token 0 for a missing row, the last stage past the end), so they
-    // carry no branches; a missing row is zeroed through its scale.
+    // Raw FP4 bytes of one stage (registers) and its scale bytes (LDS).
+    // Loads always read a valid row (token 0 for a missing row, the last
+    // stage past the end), so they carry no branches; a missing row gets
+    // zero scales.
     struct Raw {
-        u32x4 a, b;
-        uint32_t sa, sb;
+        u32x4 a, b[NBI];
+        f16x2_t sa, sb[NBI];   // the stage's two scales of each row half, decoded
     };
     const int nst = K / kFcKS;
     auto load_raw = [&](int st, Raw& R) {
         const int kk = (st < nst ? st : nst - 1) * kFcKS;
         R.a = *reinterpret_cast<const u32x4*>(xa + kk / 2);
-        R.sa = *reinterpret_cast<const uint16_t*>(xsa + kk / 16);
-        R.b = *reinterpret_cast<const u32x4*>(wb + kk / 2);
-        R.sb = *reinterpret_cast<const uint16_t*>(wsb + kk / 16);
+#pragma unroll
+        for (int i = 0; i < NBI; ++i) R.b[i] = *reinterpret_cast<const u32x4*>(wb[i] + kk / 2);
     };
-    // Word q of the stage's 16 bytes (8 elements, scale byte q / 2) of A and
-    // of B, dequantised into 16-byte chunk 4 h + q of row r of buffer `buf`.
+    // Scale bytes go through LDS in chunks of kFcSch stages (32 bytes of a
+    // row, loaded as 16 bytes by each of its two threads), double-buffered:
+    // one 16-byte request per row half per chunk instead of a 2-byte request
+    // per stage, which left most of every L2 request unused.
+    char* scl = lds + 2 * S::STAGE;
+    const int ksb = K / 16;                 // scale bytes per row (a multiple of 4)
+    struct Scl {
+        uint32_t a[4], b[NBI][4];
+    };
+    auto load_scl = [&](int c, Scl& X) {
+        const int oa = c * (kFcSch * 4) + 16 * h;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            X.a[d] = oa + 4 * d < ksb ? *reinterpret_cast<const uint32_t*>(xsrow + oa + 4 * d) : 0u;
+#pragma unroll
+        for (int i = 0; i < NBI; ++i) {
+            const int ob = c * (kFcSch * 4) + 16 * b_h[i];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                X.b[i][d] = ob + 4 * d < ksb ? *reinterpret_cast<const uint32_t*>(wsb[i] + ob + 4 * d) : 0u;
+        }
+    };
+    auto write_scl = [&](int c, const Scl& X) {
+        char* base = scl + (c & 1) * S::SCHUNK;
+        *reinterpret_cast<u32x4*>(base + r * 32 + 16 * h) =
+            a_ok ? u32x4{X.a[0], X.a[1], X.a[2], X.a[3]} : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NBI; ++i)
+            if (b_ok[i])
+                *reinterpret_cast<u32x4*>(base + (BM + b_r[i]) * 32 + 16 * b_h[i]) =
+                    u32x4{X.b[i][0], X.b[i][1], X.b[i][2], X.b[i][3]};
+    };
+    // this thread's two scales of stage st (its K half), decoded once
+    auto read_scl = [&](int st, Raw& R) {
+        const char* base = scl + ((st / kFcSch) & 1) * S::SCHUNK + 4 * (st % kFcSch);
+        R.sa = scale_pair(*reinterpret_cast<const uint16_t*>(base + r * 32 + 2 * h));
+#pragma unroll
+        for (int i = 0; i < NBI; ++i)
+            R.sb[i] = scale_pair(*reinterpret_cast<const uint16_t*>(base + (BM + b_r[i]) * 32 + 2 * b_h[i]));
+    };
+    // Word q of the stage's 16 bytes (8 elements, scale byte q / 2) of each
+    // of this thread's row halves, dequantised into 16-byte chunk 4 h + q of
+    // its row in buffer `buf`.
     auto store_word = [&](const Raw& R, int q, int buf) {
         char* A = lds + buf * S::STAGE;
-        char* B = A + kFcBM * kFcKS * 2;
+        char* B = A + BM * kFcKS * 2;
         const uint32_t wa = q == 0 ? R.a.x : q == 1 ? R.a.y : q == 2 ? R.a.z : R.a.w;
-        const uint32_t wbw = q == 0 ? R.b.x : q == 1 ? R.b.y : q == 2 ? R.b.z : R.b.w;
-        const _Float16 sA = static_cast<_Float16>(
-            a_ok ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>((R.sa >> (8 * (q >> 1))) & 0xFFu), 0) : 0.f);
-        const _Float16 sB = static_cast<_Float16>(
-            __builtin_amdgcn_cvt_f32_fp8(static_cast<int>((R.sb >> (8 * (q >> 1))) & 0xFFu), 0));
+        const _Float16 sA = q < 2 ? R.sa.x : R.sa.y;
         uint32_t d[4];
         dequant8(wa, f16x2_t{sA, sA}, d);
         *reinterpret_cast<u32x4*>(A + chunk_off(r, 4 * h + q)) = u32x4{d[0], d[1], d[2], d[3]};
-        if (b_row) {
-            dequant8(wbw, f16x2_t{sB, sB}, d);
-            *reinterpret_cast<u32x4*>(B + chunk_off(r, 4 * h + q)) = u32x4{d[0], d[1], d[2], d[3]};
+#pragma unroll
+        for (int i = 0; i < NBI; ++i) {
+            if (b_ok[i]) {
+                const u32x4 rb = R.b[i];
+                const uint32_t wbw = q == 0 ? rb.x : q == 1 ? rb.y : q == 2 ? rb.z : rb.w;
+                const _Float16 sB = q < 2 ? R.sb[i].x : R.sb[i].y;
+                dequant8(wbw, f16x2_t{sB, sB}, d);
+                *reinterpret_cast<u32x4*>(B + chunk_off(b_r[i], 4 * b_h[i] + q)) = u32x4{d[0], d[1], d[2], d[3]};
+            }
         }
     };
 
@@ -212,18 +305,35 @@ __global__ __launch_bounds__(kFcBlock) __attribute__((amdgpu_waves_per_eu(2))) v
     const int frow = lane & 31, hc = lane >> 5;
 
     // Stage s: the MFMAs on buffer s % 2 are interleaved with the
-    // dequantisation of stage s + 1 (loaded during stage s - 1) into the
-    // other buffer; stage s + 2 is loaded at the start of stage s.
-    Raw raw[2];
-    load_raw(0, raw[0]);
-    load_raw(1, raw[1]);
+    // dequantisation of stage s + 1 into the other buffer; the raw bytes of
+    // stage s + kFcRaw are loaded at the start of stage s, so a load has
+    // kFcRaw - 1 stages to arrive.
+    // Scale chunk c + 1 is loaded at stage kFcSch c (chunk 1 here) and
+    // written to LDS at stage kFcSch c + kFcSch / 2, into the buffer chunk
+    // c - 1 left (its last read was at stage kFcSch c - 2); it is first read
+    // at stage kFcSch (c + 1) - 1.
+    Raw raw[kFcRaw];
+    Scl sc;
+#pragma unroll
+    for (int i = 0; i < kFcRaw; ++i) load_raw(i, raw[i]);
+    load_scl(0, sc);
+    write_scl(0, sc);
+    if (kFcSch < nst) load_scl(1, sc);
+    lds_barrier();
+    read_scl(0, raw[0]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) store_word(raw[0], q, 0);
-    __syncthreads();
+    lds_barrier();
     auto stage = [&](int st, Raw& cur, Raw& nxt) {
-        load_raw(st + 2, cur);            // cur's bytes were dequantised during stage st - 1
+        load_raw(st + kFcRaw, cur);       // cur's bytes were dequantised during stage st - 1
+        const int c = st / kFcSch, u = st % kFcSch;
+        if ((c + 1) * kFcSch < nst) {
+            if (u == 0 && c > 0) load_scl(c + 1, sc);
+            if (u == kFcSch / 2) write_scl(c + 1, sc);
+        }
+        if (st + 1 < nst) read_scl(st + 1, nxt);
         const char* A = lds + (st & 1) * S::STAGE;
-        const char* B = A + kFcBM * kFcKS * 2;
+        const char* B = A + BM * kFcKS * 2;
 #pragma unroll
         for (int j = 0; j < kFcKS / 16; ++j) {
             f16x8_t a[MT], b[NT];
@@ -240,12 +350,19 @@ __global__ __launch_bounds__(kFcBlock) __attribute__((amdgpu_waves_per_eu(2))) v
                     acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jn], acc[i][jn], 0, 0, 0);
             if (st + 1 < nst) store_word(nxt, j, (st + 1) & 1);
         }
-        __syncthreads();
+        lds_barrier();
     };
-    for (int s = 0; s < nst; s += 2) {
-        stage(s, raw[0], raw[1]);
-        if (s + 1 < nst) stage(s + 1, raw[1], raw[0]);
+    // whole rounds of kFcRaw stages carry no conditions, so the compiler can
+    // count the loads in flight exactly (and waits only for the oldest);
+    // the remaining nst % kFcRaw stages follow
+    int s0 = 0;
+    for (; s0 + kFcRaw <= nst; s0 += kFcRaw) {
+#pragma unroll
+        for (int u = 0; u < kFcRaw; ++u) stage(s0 + u, raw[u], raw[(u + 1) % kFcRaw]);
     }
+#pragma unroll
+    for (int u = 0; u < kFcRaw - 1; ++u)
+        if (s0 + u < nst) stage(s0 + u, raw[u], raw[(u + 1) % kFcRaw]);
 
     // epilogue: y = Relu2(alpha * acc), staged in LDS as FP32 one half of the
     // rows at a time (the stage buffers are free: every wave passed the last
@@ -257,7 +374,7 @@ __global__ __launch_bounds__(kFcBlock) __attribute__((amdgpu_waves_per_eu(2))) v
     const size_t yrow_b = static_cast<size_t>(N) / 2, yrow_s = static_cast<size_t>(N) / 16;
     float* Y = reinterpret_cast<float*>(lds);
     const int half = lane >> 5;
-    constexpr int HALF_ROWS = kFcBM / 2;
+    constexpr int HALF_ROWS = BM / 2;
     constexpr int WAVE_ROWS = 32 * MT;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -276,11 +393,11 @@ __global__ __launch_bounds__(kFcBlock) __attribute__((amdgpu_waves_per_eu(2))) v
                     }
                 }
         }
-        __syncthreads();
+        lds_barrier();
         constexpr int NB = HALF_ROWS * (BN / 16);   // 16-column blocks in the half
         // consecutive lanes take consecutive rows of one column block: the
         // row stride (BN + 4 floats) puts their 16-byte reads on distinct banks
-        for (int q = tid; q < NB; q += kFcBlock) {
+        for (int q = tid; q < NB; q += S::THREADS) {
             const int row = q % HALF_ROWS, cb = q / HALF_ROWS;
             const int pr = m0 + hh * HALF_ROWS + row;
             const float4* src = reinterpret_cast<const float4*>(Y + row * S::YSTRIDE + cb * 16);
@@ -322,23 +439,31 @@ __global__ __launch_bounds__(kFcBlock) __attribute__((amdgpu_waves_per_eu(2))) v
                 y_scales[static_cast<size_t>(pr) * yrow_s + n0 / 16 + cb] = static_cast<uint8_t>(sf);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
+// Smallest row tile of any configuration: sizes the workspace's tile table.
+constexpr int kFcMinBM = 256;
+
+// Lays out the row tiles of this configuration's height, then launches the
+// GEMM over them.
 template <int WM, int WN, int MT, int NT>
 int launch_fc1(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_gs, const int32_t* perm,
-               const int32_t* offsets, const int32_t* tile_start, int k, const uint8_t* w_packed,
+               const int32_t* offsets, int32_t* tile_start, int4* tile_info, int k, const uint8_t* w_packed,
                const uint8_t* w_scales, const float* w_gs, const float* y_gs, int K, int N, int E,
                long long P, uint8_t* y_packed, uint8_t* y_scales, void* stream) {
     using S = FcShape<WM, WN, MT, NT>;
-    // row tiles over experts: at most ceil(P / BM) + E
-    const long long m_upper = (P + kFcBM - 1) / kFcBM + E;
+    static_assert(S::BM >= kFcMinBM, "the workspace holds tiles of at least kFcMinBM rows");
+    const long long m_upper = fc1_row_tiles_upper(P, E, S::BM);
     const long long tiles = m_upper * (N / S::BN);
     const long long per_xcd = (tiles + 7) / 8;
     if (per_xcd * 8 >= (1ll << 31)) return MOE_ERR_BAD_SHAPE;
-    return launch(fc1_gemm_kernel<WM, WN, MT, NT>, dim3(static_cast<unsigned>(per_xcd * 8)), dim3(kFcBlock),
-                  S::LDS, stream, x_packed, x_scales, x_gs, perm, offsets, tile_start, k, w_packed,
+    const int rc = launch(fc1_tiles_kernel, dim3(1), dim3(kFcTilesBlock), 0, stream, offsets, E,
+                          static_cast<int>(P), S::BM, static_cast<int>(m_upper), tile_start, tile_info);
+    if (rc) return rc;
+    return launch(fc1_gemm_kernel<WM, WN, MT, NT>, dim3(static_cast<unsigned>(per_xcd * 8)), dim3(S::THREADS),
+                  S::LDS, stream, x_packed, x_scales, x_gs, perm, tile_start, tile_info, k, w_packed,
                   w_scales, w_gs, y_gs, K, N, E, static_cast<int>(P), static_cast<int>(m_upper),
                   static_cast<int>(per_xcd), y_packed, y_scales);
 }
@@ -346,9 +471,20 @@ int launch_fc1(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_
 }  // namespace
 }  // namespace moe
 
-extern "C" size_t moe_expert_fc1_workspace_bytes(int E) {
-    if (E < 1 || E > MOE_MAX_EXPERTS) return 0;
-    return (static_cast<size_t>(E + 1) * sizeof(int32_t) + 255) / 256 * 256;
+namespace moe {
+namespace {
+// Workspace: tile_start [E + 1] int32, padded to 256 bytes, then tile_info
+// [fc1_row_tiles_upper] int4.
+size_t fc1_tile_start_bytes(int E) { return (static_cast<size_t>(E + 1) * sizeof(int32_t) + 255) / 256 * 256; }
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_expert_fc1_workspace_bytes(int T, int k, int E) {
+    using namespace moe;
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    const long long P = static_cast<long long>(T) * k;
+    if (P >= (1ll << 31)) return 0;
+    return fc1_tile_start_bytes(E) + static_cast<size_t>(fc1_row_tiles_upper(P, E, kFcMinBM)) * sizeof(int4);
 }
 
 extern "C" int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales,
@@ -372,29 +508,23 @@ extern "C" int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_sc
     if (!all_aligned16(x_packed, w_packed, y_packed, y_scales)) return MOE_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(x_scales) | reinterpret_cast<uintptr_t>(w_scales)) & 3u)
         return MOE_ERR_ALIGN;
-    const size_t need = moe_expert_fc1_workspace_bytes(E);
+    const size_t need = moe_expert_fc1_workspace_bytes(T, k, E);
     if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MOE_ERR_ALIGN;
     int32_t* tile_start = static_cast<int32_t*>(workspace);
+    int4* tile_info = reinterpret_cast<int4*>(static_cast<char*>(workspace) + fc1_tile_start_bytes(E));
 
-    int rc = launch(fc1_tiles_kernel, dim3(1), dim3(kFcBlock), 0, stream, offsets, E, tile_start);
-    if (rc) return rc;
     const int cap = device_cu_count() * 8;
     const long long fill_vec = P * (N / 32);
     const int gf = static_cast<int>(fill_vec / 256 + 1 < cap ? fill_vec / 256 + 1 : cap);
-    rc = launch(fc1_fill_kernel, dim3(gf), dim3(256), 0, stream, offsets, E, static_cast<int>(P), N,
+    const int rc = launch(fc1_fill_kernel, dim3(gf), dim3(256), 0, stream, offsets, E, static_cast<int>(P), N,
                 reinterpret_cast<u32x4*>(y_packed), reinterpret_cast<uint32_t*>(y_scales));
     if (rc) return rc;
     // widest column tile that divides N: 192, 256 or 128 columns
-    if (N % 192 == 0)
-        return launch_fc1<4, 2, 2, 3>(x_packed, x_scales, x_global_scale, perm, offsets, tile_start, k,
-                                      w_packed, w_scales, w_global_scale, y_global_scale, K, N, E, P,
-                                      y_packed, y_scales, stream);
-    if (N % 256 == 0)
-        return launch_fc1<2, 4, 4, 2>(x_packed, x_scales, x_global_scale, perm, offsets, tile_start, k,
-                                      w_packed, w_scales, w_global_scale, y_global_scale, K, N, E, P,
-                                      y_packed, y_scales, stream);
-    return launch_fc1<4, 2, 2, 2>(x_packed, x_scales, x_global_scale, perm, offsets, tile_start, k,
-                                  w_packed, w_scales, w_global_scale, y_global_scale, K, N, E, P,
-                                  y_packed, y_scales, stream);
+#define FC1_ARGS x_packed, x_scales, x_global_scale, perm, offsets, tile_start, tile_info, k, w_packed, \
+                 w_scales, w_global_scale, y_global_scale, K, N, E, P, y_packed, y_scales, stream
+    if (N % 192 == 0) return launch_fc1<4, 2, 2, 3>(FC1_ARGS);
+    if (N % 256 == 0) return launch_fc1<2, 4, 4, 2>(FC1_ARGS);
+    return launch_fc1<4, 2, 2, 2>(FC1_ARGS);
+#undef FC1_ARGS
 }

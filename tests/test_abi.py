@@ -125,9 +125,14 @@ def test_dispatch_rejects_before_launch(lib):
 
 def test_expert_fc1_rejects_before_launch(lib):
     f = lib.moe_expert_fc1_nvfp4
-    ws = lib.moe_expert_fc1_workspace_bytes(8)
-    assert ws >= 9 * 4 and ws % 256 == 0
-    assert lib.moe_expert_fc1_workspace_bytes(0) == 0
+    ws = lib.moe_expert_fc1_workspace_bytes(4, 2, 8)
+    # tile starts (9 int32, padded to 256 bytes) + one record per possible row tile
+    assert ws == 256 + 16 * (1 + 8)   # tiles of 256 rows
+    assert lib.moe_expert_fc1_workspace_bytes(4, 2, 0) == 0
+    assert lib.moe_expert_fc1_workspace_bytes(-1, 2, 8) == 0
+    assert lib.moe_expert_fc1_workspace_bytes(4, 0, 8) == 0
+    assert lib.moe_expert_fc1_workspace_bytes(1 << 30, 2, 8) == 0
+    assert lib.moe_expert_fc1_workspace_bytes(0, 2, 8) == 256 + 16 * 8
     args = lambda T=4, k=2, K=128, N=256, E=8, ws_b=ws, x=FAKE: (
         x, FAKE, FAKE, FAKE, FAKE, T, k, FAKE, FAKE, FAKE, FAKE, K, N, E, FAKE, FAKE, FAKE, ws_b, None)
     assert f(*args(K=96)) == -2        # K % 64
