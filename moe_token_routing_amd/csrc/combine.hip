@@ -30,7 +30,11 @@ struct CombineCfg {
     static constexpr int G = VPT >= 8 ? 2 : (VPT >= 4 ? 4 : 8);
 };
 
-template <int VPT>
+// WHOLE: one token per block (tpt = kRowBlock) and every thread owns exactly
+// VPT vectors (H / 8 = VPT kRowBlock). The token, its slots and their
+// validity are then the same for the whole block, so they live in scalar
+// registers and the per-vector bounds checks disappear.
+template <int VPT, bool WHOLE>
 __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     const u32x4* __restrict__ expert_out, int R, const int32_t* __restrict__ slots,
     const float* __restrict__ topk_w, const float* __restrict__ norm_w, float gain_center,
@@ -52,9 +56,10 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     }
     __syncthreads();
 
-    const int tokens_per_block = kRowBlock / tpt;
-    const int sub = threadIdx.x / tpt;
-    const int tid = threadIdx.x - sub * tpt;
+    const int tokens_per_block = WHOLE ? 1 : kRowBlock / tpt;
+    const int sub = WHOLE ? 0 : threadIdx.x / tpt;
+    const int tid = WHOLE ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) - sub * tpt;
+    if (WHOLE) tpt = kRowBlock;
     const float hf = static_cast<float>(H);
 
     for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
 #pragma unroll
                     for (int i = 0; i < VPT; ++i) {
                         const int v = tid + i * tpt;
-                        if (v < nvec) x[g][i] = load_nt(&row[v]);
+                        if (WHOLE || v < nvec) x[g][i] = load_nt(&row[v]);
                     }
                 }
             }
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
                 if (ok[g]) {
 #pragma unroll
                     for (int i = 0; i < VPT; ++i) {
-                        if (tid + i * tpt < nvec) {
+                        if (WHOLE || tid + i * tpt < nvec) {
                             s = dot2_sq(x[g][i].x, s);
                             s = dot2_sq(x[g][i].y, s);
                             s = dot2_sq(x[g][i].z, s);
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
                     const int v = tid + i * tpt;
-                    if (v >= nvec) continue;
+                    if (!WHOLE && v >= nvec) continue;
                     const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
                     const float4 ga = gain_lo[v], gb = gain_hi[v];
                     const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = tid + i * tpt;
-                if (v < nvec) {
+                if (WHOLE || v < nvec) {
                     u32x4 o;
                     o.x = cvt_pk_bf16(acc[i][0], acc[i][1]);
                     o.y = cvt_pk_bf16(acc[i][2], acc[i][3]);
@@ -147,16 +152,16 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     }
 }
 
-template <int VPT>
+template <int VPT, bool WHOLE>
 int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
                    const float* norm_w, float gain_center, float eps, int T, int H, int k,
                    const RowGeom& geo, uint16_t* out, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
     const size_t lds = sizeof(float) * static_cast<size_t>(H);
-    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT>, kRowBlock, lds);
+    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT, WHOLE>, kRowBlock, lds);
     const int grid = needed < cap ? needed : cap;
-    return launch(combine_kernel<VPT>, dim3(grid), dim3(kRowBlock), lds, stream,
+    return launch(combine_kernel<VPT, WHOLE>, dim3(grid), dim3(kRowBlock), lds, stream,
                   reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
                   gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
 }
@@ -180,11 +185,14 @@ extern "C" int moe_combine(const uint16_t* expert_out, int R, const int32_t* slo
     const RowGeom geo = row_geom(H);
     int vpt = 1;
     while (vpt < geo.vpt) vpt <<= 1;
+    const bool whole = geo.tpt == kRowBlock && geo.nvec == vpt * kRowBlock;
+#define MOE_COMBINE(V, W) launch_combine<V, W>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream)
     switch (vpt) {
-        case 1: return launch_combine<1>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
-        case 2: return launch_combine<2>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
-        case 4: return launch_combine<4>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
-        case 8: return launch_combine<8>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream);
+        case 1: return whole ? MOE_COMBINE(1, true) : MOE_COMBINE(1, false);
+        case 2: return whole ? MOE_COMBINE(2, true) : MOE_COMBINE(2, false);
+        case 4: return whole ? MOE_COMBINE(4, true) : MOE_COMBINE(4, false);
+        case 8: return whole ? MOE_COMBINE(8, true) : MOE_COMBINE(8, false);
         default: return MOE_ERR_BAD_SHAPE;
     }
+#undef MOE_COMBINE
 }

@@ -36,16 +36,20 @@ __device__ __forceinline__ float round_to_bf16(float f) {
 // neighbouring 16-byte vectors, so its scale is computed once, by the lane
 // that holds it. A 256-thread block serves 256 / tpt tokens, tpt threads per
 // token (tpt = the power of two >= H/16, at most 256), BPT blocks per thread.
-template <int BPT>
+// WHOLE: one token per block and exactly BPT blocks per thread (H / 16 =
+// BPT kRowBlock), so the token is the same for the whole block and the
+// per-block bounds checks disappear.
+template <int BPT, bool WHOLE>
 __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
     const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
     uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     __shared__ float red[kRowBlock / kWave];
     const int nblk = H >> 4;
-    const int tokens_per_block = kRowBlock / tpt;
-    const int sub = threadIdx.x / tpt;
-    const int tid = threadIdx.x - sub * tpt;
+    if (WHOLE) tpt = kRowBlock;
+    const int tokens_per_block = WHOLE ? 1 : kRowBlock / tpt;
+    const int sub = WHOLE ? 0 : threadIdx.x / tpt;
+    const int tid = WHOLE ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) - sub * tpt;
     const float hf = static_cast<float>(H);
     const float gs = *global_scale;
     const float rcp_gs = 1.0f / gs;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
         src[i] = static_cast<size_t>(rb) * T * shard8 + (v - rb * shard8);
 #pragma unroll
         for (int e = 0; e < 16; ++e) gain[i][e] = 0.f;
-        if (b < nblk) {
+        if (WHOLE || b < nblk) {
             const float4* g4 = reinterpret_cast<const float4*>(norm_w) + 4 * b;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             u32x4 a = u32x4{0u, 0u, 0u, 0u}, c = u32x4{0u, 0u, 0u, 0u};
-            if (tok_ok && tid + i * tpt < nblk) {
+            if (WHOLE || (tok_ok && tid + i * tpt < nblk)) {
                 const u32x4* p = &x[src[i] + static_cast<size_t>(t) * shard8];
                 a = load_nt(p);
                 c = load_nt(p + 1);
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
                     w1 |= e2m1_code(bf16_hi(yp[q + 4]) * outs) << (8 * q + 4);
                 }
             }
-            if (tok_ok && b < nblk) {
+            if (WHOLE || (tok_ok && b < nblk)) {
                 packed[static_cast<size_t>(t) * nblk + b] = make_uint2(w0, w1);
                 scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf);
             }
@@ -164,16 +168,16 @@ inline BlockGeom block_geom(int H) {
     return g;
 }
 
-template <int BPT>
+template <int BPT, bool WHOLE>
 int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
                       const float* global_scale, int T, int H, int shard, const BlockGeom& geo,
                       uint8_t* packed, uint8_t* scales, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
     // as many blocks as fit on the GPU at once; each loops over its tokens
-    const int cap = device_cu_count() * resident_blocks(norm_quant_kernel<BPT>, kRowBlock, 0);
+    const int cap = device_cu_count() * resident_blocks(norm_quant_kernel<BPT, WHOLE>, kRowBlock, 0);
     const int grid = needed < cap ? needed : cap;
-    return launch(norm_quant_kernel<BPT>, dim3(grid), dim3(kRowBlock), 0, stream,
+    return launch(norm_quant_kernel<BPT, WHOLE>, dim3(grid), dim3(kRowBlock), 0, stream,
                   reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
                   shard / 8, geo.tpt, reinterpret_cast<uint2*>(packed), scales);
 }
@@ -193,13 +197,16 @@ extern "C" int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, con
     if (!x || !norm_w || !global_scale || !packed || !scales) return MOE_ERR_NULL_ARG;
     if (!all_aligned16(x, norm_w, packed, scales)) return MOE_ERR_ALIGN;
     const BlockGeom geo = block_geom(H);
+    const bool whole = geo.tpt == kRowBlock && H / 16 == geo.bpt * kRowBlock;
+#define MOE_NQ(B, W) launch_norm_quant<B, W>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream)
     switch (geo.bpt) {
-        case 1: return launch_norm_quant<1>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
-        case 2: return launch_norm_quant<2>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
-        case 3: return launch_norm_quant<3>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
-        case 4: return launch_norm_quant<4>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream);
+        case 1: return whole ? MOE_NQ(1, true) : MOE_NQ(1, false);
+        case 2: return whole ? MOE_NQ(2, true) : MOE_NQ(2, false);
+        case 3: return whole ? MOE_NQ(3, true) : MOE_NQ(3, false);
+        case 4: return whole ? MOE_NQ(4, true) : MOE_NQ(4, false);
         default: return MOE_ERR_BAD_SHAPE;
     }
+#undef MOE_NQ
 }
 
 extern "C" int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, float gain_center,
