@@ -31,8 +31,10 @@
 //    16-byte record per tile: expert, first row, row end), so a GEMM block
 //    learns its tile from one load; the grid is an upper bound, blocks past
 //    the last tile leave at once. Blocks are
-//    remapped so that each XCD walks a contiguous run of (column tile,
-//    expert, row tile), keeping an expert's weight slice in its L2.
+//    remapped so that each XCD walks a contiguous run of (row tile, column
+//    tile) with the column tile fastest: the blocks of one gathered A tile
+//    run side by side and find it in their XCD's L2, and so do an expert's
+//    weights across its row tiles.
 //  * Epilogue: alpha * acc, Relu2, staged in LDS as FP32 half a tile at a
 //    time, then each thread quantises 16-column blocks with the pre-expert quantiser's FP32 steps
 //    (hardware E4M3 and FP4 conversions, as there).
@@ -175,19 +177,27 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const float* __restrict__ x_gs, const int32_t* __restrict__ perm, const int32_t* __restrict__ tile_start,
     const int4* __restrict__ tile_info, int k, const uint8_t* __restrict__ w_packed,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_gs, const float* __restrict__ y_gs,
-    int K, int N, int E, int n_pos, int m_upper, int per_xcd, uint8_t* __restrict__ y_packed,
+    int K, int N, int E, int n_pos, int m_upper, uint8_t* __restrict__ y_packed,
     uint8_t* __restrict__ y_scales) {
     using S = FcShape<WM, WN, MT, NT>;
     constexpr int BM = S::BM, BN = S::BN, NBI = S::NBI;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-    // XCD-contiguous logical tile index: (column tile, row tile over experts)
-    const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    const int nt = logical / m_upper;
-    const int mt = logical - nt * m_upper;   // < m_upper: tile_info[mt] is in bounds
-    const int total = tile_start[E];
+    // Logical tile (row tile over experts, column tile), column tile fastest,
+    // split into eight contiguous runs, one per XCD (block b runs on XCD
+    // b % 8): an XCD's neighbouring blocks share the gathered A tile, and an
+    // expert's weights, in its L2. The runs cover only the row tiles that
+    // exist (the grid is sized for the upper bound m_upper).
+    const int total = min(tile_start[E], m_upper);
+    const int ntn = N / BN;
+    const int per = (total * ntn + 7) / 8;
+    const int idx = blockIdx.x / 8;
+    if (idx >= per) return;
+    const int logical = (blockIdx.x % 8) * per + idx;
+    const int mt = logical / ntn;
+    if (mt >= total) return;
+    const int nt = logical - mt * ntn;
     const int4 info = tile_info[mt];
-    if (nt >= N / BN || mt >= total) return;
     const int e = info.x, m0 = info.y, row_end = info.z;
     const int n0 = nt * BN;
 
@@ -465,7 +475,7 @@ int launch_fc1(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_
     return launch(fc1_gemm_kernel<WM, WN, MT, NT>, dim3(static_cast<unsigned>(per_xcd * 8)), dim3(S::THREADS),
                   S::LDS, stream, x_packed, x_scales, x_gs, perm, tile_start, tile_info, k, w_packed,
                   w_scales, w_gs, y_gs, K, N, E, static_cast<int>(P), static_cast<int>(m_upper),
-                  static_cast<int>(per_xcd), y_packed, y_scales);
+                  y_packed, y_scales);
 }
 
 }  // namespace
