@@ -35,8 +35,11 @@
 //    tile) with the column tile fastest: the blocks of one gathered A tile
 //    run side by side and find it in their XCD's L2, and so do an expert's
 //    weights across its row tiles.
-//  * Epilogue: alpha * acc, Relu2, staged in LDS as FP32 half a tile at a
-//    time, then each thread quantises 16-column blocks with the pre-expert quantiser's FP32 steps
+//  * Epilogue straight from the accumulators: the MFMAs take the weight
+//    rows as their first operand, so each lane holds 16 output columns of
+//    one grouped row, half of two 16-column blocks; the two lanes holding a
+//    block meet through v_permlane32_swap for its maximum and its codes.
+//    alpha * acc, Relu2, then the pre-expert quantiser's FP32 steps
 //    (hardware E4M3 and FP4 conversions, as there).
 #include <cmath>
 
@@ -69,9 +72,7 @@ struct FcShape {
     static constexpr int STAGE = (BM + BN) * kFcKS * 2;              // A and B tiles, FP16 bytes
     static constexpr int SCHUNK = (BM + BN) * kFcSch * 4;             // one scale chunk of every row
     static constexpr size_t MAIN = 2 * static_cast<size_t>(STAGE) + 2 * static_cast<size_t>(SCHUNK);
-    static constexpr int YSTRIDE = BN + 4;                            // floats per staged output row
-    static constexpr size_t YBYTES = static_cast<size_t>(BM / 2) * YSTRIDE * 4;   // half the rows
-    static constexpr size_t LDS = MAIN > YBYTES ? MAIN : YBYTES;
+    static constexpr size_t LDS = MAIN;
 };
 
 // Row tiles of `bm` rows over experts: at most ceil(P / bm) + E (each
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
             for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int jn = 0; jn < NT; ++jn)
-                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jn], acc[i][jn], 0, 0, 0);
+                    acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[jn], a[i], acc[i][jn], 0, 0, 0);
             if (st + 1 < nst) store_word(nxt, j, (st + 1) & 1);
         }
         lds_barrier();
@@ -374,82 +375,68 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     for (int u = 0; u < kFcRaw - 1; ++u)
         if (s0 + u < nst) stage(s0 + u, raw[u], raw[(u + 1) % kFcRaw]);
 
-    // epilogue: y = Relu2(alpha * acc), staged in LDS as FP32 one half of the
-    // rows at a time (the stage buffers are free: every wave passed the last
-    // barrier after its last MFMA reads), then quantised 16 columns at a time
+    // Epilogue, from the accumulators (no LDS): the MFMAs ran with the weight
+    // rows as the first operand, so lane l of accumulator (i, jn) holds
+    // grouped row (l & 31) of row tile i and output columns 8 (q >> 2) +
+    // 4 (l >> 5) + (q & 3), q < 16, of column tile jn. A 16-column block is
+    // then values q = 8 blk .. 8 blk + 7 of lanes l and l + 32, which meet
+    // through one v_permlane32_swap for the block maximum and one for the
+    // codes. y = Relu2(alpha acc), then the pre-expert quantiser's FP32 steps.
     const float alpha = 1.0f / (*x_gs * w_gs[e]);
     const float gs = *y_gs;
     const float rcp_gs = 1.0f / gs;
     constexpr float kRcp6 = 1.0f / 6.0f;
     const size_t yrow_b = static_cast<size_t>(N) / 2, yrow_s = static_cast<size_t>(N) / 16;
-    float* Y = reinterpret_cast<float*>(lds);
     const int half = lane >> 5;
-    constexpr int HALF_ROWS = BM / 2;
-    constexpr int WAVE_ROWS = 32 * MT;
+    // lane pair (l, l + 32) -> the block's 8 code bytes: the lower lane
+    // writes bytes 0-3 (its codes 0-3, the upper lane's 4-7), the upper lane
+    // bytes 4-7 (its codes 12-15 after the lower lane's 8-11)
+    const uint32_t sel = half ? 0x07060302u : 0x05040100u;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        if (wm * WAVE_ROWS / HALF_ROWS == hh) {
+    for (int i = 0; i < MT; ++i) {
+        const int pr = m0 + wm * 32 * MT + i * 32 + (lane & 31);
+        const bool row_ok = pr >= 0 && pr < row_end;
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
+        for (int jn = 0; jn < NT; ++jn) {
+            const int c0 = n0 + wn * 32 * NT + jn * 32;
 #pragma unroll
-                for (int jn = 0; jn < NT; ++jn) {
-                    const int col = wn * 32 * NT + jn * 32 + (lane & 31);
+            for (int blk = 0; blk < 2; ++blk) {
+                float y[8];
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int row = wm * WAVE_ROWS + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3) - hh * HALF_ROWS;
-                        const float v = alpha * acc[i][jn][q];
-                        const float rl = v > 0.f ? v : 0.f;
-                        Y[row * S::YSTRIDE + col] = rl * rl;
-                    }
+                for (int u = 0; u < 8; ++u) {
+                    const float v = alpha * acc[i][jn][8 * blk + u];
+                    const float rl = v > 0.f ? v : 0.f;
+                    y[u] = rl * rl;
                 }
-        }
-        lds_barrier();
-        constexpr int NB = HALF_ROWS * (BN / 16);   // 16-column blocks in the half
-        // consecutive lanes take consecutive rows of one column block: the
-        // row stride (BN + 4 floats) puts their 16-byte reads on distinct banks
-        for (int q = tid; q < NB; q += S::THREADS) {
-            const int row = q % HALF_ROWS, cb = q / HALF_ROWS;
-            const int pr = m0 + hh * HALF_ROWS + row;
-            const float4* src = reinterpret_cast<const float4*>(Y + row * S::YSTRIDE + cb * 16);
-            float y[16];
+                float lm = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+                const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+                const float amax = fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));   // y >= 0
+                const float sc = gs * (amax * kRcp6);
+                const uint32_t sf = e4m3_scale_code(sc);
+                const float sf_f = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sf), 0);
+                const float d = sf_f * rcp_gs;
+                const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
+                uint32_t w = 0;
+                if (amax < INFINITY && fabsf(outs) < INFINITY) {
+                    // y >= 0, so q = y * out is never -0; the hardware conversion
+                    // with unit scale rounds finite values to nearest even and saturates
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * outs, y[1] * outs, 1.0f, 0);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * outs, y[3] * outs, 1.0f, 1);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * outs, y[5] * outs, 1.0f, 2);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * outs, y[7] * outs, 1.0f, 3);
+                } else {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float4 f = src[v];
-                y[4 * v] = f.x; y[4 * v + 1] = f.y; y[4 * v + 2] = f.z; y[4 * v + 3] = f.w;
-            }
-            float amax = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) amax = fmaxf(amax, y[v]);   // y >= 0
-            const float sc = gs * (amax * kRcp6);
-            const uint32_t sf = e4m3_scale_code(sc);
-            const float sf_f = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sf), 0);
-            const float d = sf_f * rcp_gs;
-            const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
-            uint32_t w0 = 0, w1 = 0;
-            if (amax < INFINITY && fabsf(outs) < INFINITY) {
-                // y >= 0, so q = y * out is never -0; the hardware conversion
-                // with unit scale rounds finite values to nearest even and saturates
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0] * outs, y[1] * outs, 1.0f, 0);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[2] * outs, y[3] * outs, 1.0f, 1);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[4] * outs, y[5] * outs, 1.0f, 2);
-                w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[6] * outs, y[7] * outs, 1.0f, 3);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[8] * outs, y[9] * outs, 1.0f, 0);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10] * outs, y[11] * outs, 1.0f, 1);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12] * outs, y[13] * outs, 1.0f, 2);
-                w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14] * outs, y[15] * outs, 1.0f, 3);
-            } else {
-#pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    w0 |= e2m1_code(y[v] * outs) << (4 * v);
-                    w1 |= e2m1_code(y[8 + v] * outs) << (4 * v);
+                    for (int u = 0; u < 8; ++u) w |= e2m1_code(y[u] * outs) << (4 * u);
+                }
+                const auto ws = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+                const uint32_t word = __builtin_amdgcn_perm(ws[1], ws[0], sel);
+                if (row_ok) {
+                    const int cb = c0 + 16 * blk;
+                    *reinterpret_cast<uint32_t*>(y_packed + static_cast<size_t>(pr) * yrow_b + cb / 2 + 4 * half) = word;
+                    if (half == 0) y_scales[static_cast<size_t>(pr) * yrow_s + cb / 16] = static_cast<uint8_t>(sf);
                 }
             }
-            if (pr >= 0 && pr < row_end) {
-                *reinterpret_cast<uint2*>(y_packed + static_cast<size_t>(pr) * yrow_b + (n0 + cb * 16) / 2) = make_uint2(w0, w1);
-                y_scales[static_cast<size_t>(pr) * yrow_s + n0 / 16 + cb] = static_cast<uint8_t>(sf);
-            }
         }
-        lds_barrier();
     }
 }
 
