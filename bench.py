@@ -161,7 +161,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="prefill")
-    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
