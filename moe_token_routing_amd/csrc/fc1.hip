@@ -21,11 +21,11 @@
 //    are applied once, as alpha = 1 / (gs_x * gs_w[e]) in the epilogue.
 //  * Block tile 256 grouped rows x 192 (or 256, or 128) output columns,
 //    eight waves, so each dequantised row feeds more MFMAs.
-//    K advances in stages of 64: the raw FP4 bytes and scale bytes of the
-//    next stage are loaded into registers while the MFMAs of this stage run,
-//    then dequantised into the other half of a double-buffered LDS tile
-//    (rows of 128 bytes, 16-byte chunks XOR-swizzled by row pair, so neither
-//    the stores nor the fragment reads conflict on LDS banks).
+//    K advances in stages of 64: the raw FP4 bytes of a stage are loaded
+//    into registers two stages ahead (its scale bytes through LDS, below)
+//    and dequantised, while the MFMAs of the stage before run, into the
+//    other half of a double-buffered LDS tile (rows of 128 bytes, 16-byte
+//    chunks XOR-swizzled by row pair).
 //  * The row tiles of each expert are laid out from `offsets` by a one-block
 //    kernel (exclusive prefix of ceil(rows / 256) over experts, and one
 //    16-byte record per tile: expert, first row, row end), so a GEMM block
@@ -167,9 +167,10 @@ __device__ __forceinline__ f16x2_t scale_pair(uint32_t two) {
 }
 
 // Row `row` of a stage tile is 128 bytes, eight 16-byte chunks; chunk c sits
-// at c ^ ((row >> 1) & 7): the MFMA fragment reads (16 consecutive rows, one
-// chunk) and the dequantised stores (8 rows x 2 chunks) then touch 16
-// distinct 16-byte bank groups in each group of 16 lanes.
+// at c ^ ((row >> 1) & 7). Measured on gfx950 (bank-conflict counters): the
+// MFMA fragment reads do not conflict; the 16-byte dequantised stores take
+// about 8 conflict cycles each. c ^ ((row ^ (row >> 3)) & 7) is free of
+// conflicts for both, yet the kernel ran 7% slower with it.
 __device__ __forceinline__ int chunk_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 template <int WM, int WN, int MT, int NT>

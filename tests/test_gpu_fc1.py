@@ -67,6 +67,8 @@ def _case(T, k, E, K, N, seed, invalid=0.0, skew=None):
     (37, 3, 5, 128, 256, 0.1, None),            # ragged tiles, invalid slots
     (300, 2, 4, 64, 128, 0.0, [10, 0, 1, 3]),   # an empty expert, one expert over several tiles
     (64, 4, 16, 256, 384, 0.0, None),           # many small experts
+    (40, 2, 3, 576, 384, 0.0, None),            # 9 K stages: a second scale chunk of one stage
+    (33, 3, 5, 1088, 256, 0.05, None),          # 17 K stages: a third chunk, a partial scale row
 ])
 def test_fc1_small(T, k, E, K, N, invalid, skew):
     args = _case(T, k, E, K, N, seed=T + E, invalid=invalid, skew=skew)
