@@ -69,6 +69,7 @@ def _case(T, k, E, K, N, seed, invalid=0.0, skew=None):
     (64, 4, 16, 256, 384, 0.0, None),           # many small experts
     (40, 2, 3, 576, 384, 0.0, None),            # 9 K stages: a second scale chunk of one stage
     (33, 3, 5, 1088, 256, 0.05, None),          # 17 K stages: a third chunk, a partial scale row
+    (9, 2, 2, 16384, 128, 0.0, None),           # the largest K: 256 stages, 32 scale chunks
 ])
 def test_fc1_small(T, k, E, K, N, invalid, skew):
     args = _case(T, k, E, K, N, seed=T + E, invalid=invalid, skew=skew)
