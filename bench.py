@@ -77,15 +77,15 @@ def source_digest(path: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per combine launch from the committed counter summary, if it
-    was taken on the current combine source."""
+    was taken on this workload and on the current combine source."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_digest") != source_digest(COMBINE_SRC):
+    if d.get("workload") != workload or d.get("source_digest") != source_digest(COMBINE_SRC):
         return None
     return d.get("bytes_per_launch")
 
@@ -98,7 +98,7 @@ def cpu_baseline(w, sample_tokens: int):
     import workloads as wl
     from threadpoolctl import threadpool_limits
 
-    S = sample_tokens
+    S = min(sample_tokens, w.T)
     hidden = wl.hidden(w, S)
     W, bias, mask = wl.router_weight(w), wl.bias(w), wl.token_mask(w, S)
     x, qw, cg = wl.quant_input(w, S), wl.quant_gain(w), wl.combine_gain(w)
@@ -434,7 +434,7 @@ def main():
         "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(w.name)},
         "cpu_baseline": None,
     }
     if args.cpu_sample > 0:

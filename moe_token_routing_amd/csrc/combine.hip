@@ -30,11 +30,12 @@ struct CombineCfg {
     static constexpr int G = VPT >= 8 ? 2 : (VPT >= 4 ? 4 : 8);
 };
 
-// WHOLE: one token per block (tpt = kRowBlock) and every thread owns exactly
-// VPT vectors (H / 8 = VPT kRowBlock). The token, its slots and their
-// validity are then the same for the whole block, so they live in scalar
-// registers and the per-vector bounds checks disappear.
-template <int VPT, bool WHOLE>
+// TPT = 0: tpt threads per token, any power of two up to kRowBlock, with
+// bounds checks. TPT = kWave or kRowBlock: one token per wave or per block
+// and every thread owns exactly VPT vectors (H / 8 = VPT TPT). The token,
+// its slots and their validity are then the same for the whole wave, so they
+// live in scalar registers and the per-vector bounds checks disappear.
+template <int VPT, int TPT>
 __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     const u32x4* __restrict__ expert_out, int R, const int32_t* __restrict__ slots,
     const float* __restrict__ topk_w, const float* __restrict__ norm_w, float gain_center,
@@ -56,10 +57,13 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     }
     __syncthreads();
 
-    const int tokens_per_block = WHOLE ? 1 : kRowBlock / tpt;
-    const int sub = WHOLE ? 0 : threadIdx.x / tpt;
-    const int tid = WHOLE ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) - sub * tpt;
-    if (WHOLE) tpt = kRowBlock;
+    constexpr bool WHOLE = TPT != 0;
+    if (WHOLE) tpt = TPT;
+    const int tokens_per_block = kRowBlock / tpt;
+    // with TPT a multiple of the wave, a wave's lanes share one token
+    const int sub = WHOLE ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / TPT)
+                          : static_cast<int>(threadIdx.x) / tpt;
+    const int tid = static_cast<int>(threadIdx.x) - sub * tpt;
     const float hf = static_cast<float>(H);
 
     for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
@@ -152,16 +156,16 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     }
 }
 
-template <int VPT, bool WHOLE>
+template <int VPT, int TPT>
 int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
                    const float* norm_w, float gain_center, float eps, int T, int H, int k,
                    const RowGeom& geo, uint16_t* out, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
     const size_t lds = sizeof(float) * static_cast<size_t>(H);
-    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT, WHOLE>, kRowBlock, lds);
+    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT, TPT>, kRowBlock, lds);
     const int grid = needed < cap ? needed : cap;
-    return launch(combine_kernel<VPT, WHOLE>, dim3(grid), dim3(kRowBlock), lds, stream,
+    return launch(combine_kernel<VPT, TPT>, dim3(grid), dim3(kRowBlock), lds, stream,
                   reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
                   gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
 }
@@ -182,17 +186,29 @@ extern "C" int moe_combine(const uint16_t* expert_out, int R, const int32_t* slo
     if (T == 0) return MOE_OK;
     if (!slots || !topk_w || !norm_w || !out || (R > 0 && !expert_out)) return MOE_ERR_NULL_ARG;
     if (!all_aligned16(expert_out, slots, topk_w, norm_w, out)) return MOE_ERR_ALIGN;
-    const RowGeom geo = row_geom(H);
+    RowGeom geo = row_geom(H);
+    // rows of at most 128 vectors (H <= 1024): one wave per token, so the
+    // token's sums of squares never meet in LDS (measured at H 1024, k 22:
+    // 446 -> 395 us); wider rows keep the whole block (one wave per token
+    // was slower at H 4096)
+    if (geo.nvec <= 2 * kWave && geo.tpt > kWave) {
+        geo.tpt = kWave;
+        geo.vpt = (geo.nvec + kWave - 1) / kWave;
+    }
     int vpt = 1;
     while (vpt < geo.vpt) vpt <<= 1;
-    const bool whole = geo.tpt == kRowBlock && geo.nvec == vpt * kRowBlock;
-#define MOE_COMBINE(V, W) launch_combine<V, W>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream)
+    const int tpt_whole = (geo.tpt == kRowBlock || geo.tpt == kWave) && geo.nvec == vpt * geo.tpt ? geo.tpt : 0;
+#define MOE_COMBINE(V) (tpt_whole == kRowBlock ? launch_combine<V, kRowBlock>(MOE_COMBINE_ARGS) \
+                        : tpt_whole == kWave   ? launch_combine<V, kWave>(MOE_COMBINE_ARGS)     \
+                                               : launch_combine<V, 0>(MOE_COMBINE_ARGS))
+#define MOE_COMBINE_ARGS expert_out, R, slots, topk_w, norm_w, gain_center, eps, T, H, k, geo, out, stream
     switch (vpt) {
-        case 1: return whole ? MOE_COMBINE(1, true) : MOE_COMBINE(1, false);
-        case 2: return whole ? MOE_COMBINE(2, true) : MOE_COMBINE(2, false);
-        case 4: return whole ? MOE_COMBINE(4, true) : MOE_COMBINE(4, false);
-        case 8: return whole ? MOE_COMBINE(8, true) : MOE_COMBINE(8, false);
+        case 1: return MOE_COMBINE(1);
+        case 2: return MOE_COMBINE(2);
+        case 4: return MOE_COMBINE(4);
+        case 8: return MOE_COMBINE(8);
         default: return MOE_ERR_BAD_SHAPE;
     }
+#undef MOE_COMBINE_ARGS
 #undef MOE_COMBINE
 }
