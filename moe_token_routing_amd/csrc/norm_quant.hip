@@ -36,20 +36,24 @@ __device__ __forceinline__ float round_to_bf16(float f) {
 // neighbouring 16-byte vectors, so its scale is computed once, by the lane
 // that holds it. A 256-thread block serves 256 / tpt tokens, tpt threads per
 // token (tpt = the power of two >= H/16, at most 256), BPT blocks per thread.
-// WHOLE: one token per block and exactly BPT blocks per thread (H / 16 =
-// BPT kRowBlock), so the token is the same for the whole block and the
-// per-block bounds checks disappear.
-template <int BPT, bool WHOLE>
+// TPT = 0: tpt threads per token, with bounds checks. TPT = kWave or
+// kRowBlock: one token per wave or per block and exactly BPT blocks per
+// thread (H / 16 = BPT TPT), so the token is the same for the whole wave
+// and the per-block bounds checks disappear.
+template <int BPT, int TPT>
 __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
     const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
     uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     __shared__ float red[kRowBlock / kWave];
     const int nblk = H >> 4;
-    if (WHOLE) tpt = kRowBlock;
-    const int tokens_per_block = WHOLE ? 1 : kRowBlock / tpt;
-    const int sub = WHOLE ? 0 : threadIdx.x / tpt;
-    const int tid = WHOLE ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) - sub * tpt;
+    constexpr bool WHOLE = TPT != 0;
+    if (WHOLE) tpt = TPT;
+    const int tokens_per_block = kRowBlock / tpt;
+    // with TPT a multiple of the wave, a wave's lanes share one token
+    const int sub = WHOLE ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / TPT)
+                          : static_cast<int>(threadIdx.x) / tpt;
+    const int tid = static_cast<int>(threadIdx.x) - sub * tpt;
     const float hf = static_cast<float>(H);
     const float gs = *global_scale;
     const float rcp_gs = 1.0f / gs;
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             u32x4 a = u32x4{0u, 0u, 0u, 0u}, c = u32x4{0u, 0u, 0u, 0u};
-            if (WHOLE || (tok_ok && tid + i * tpt < nblk)) {
+            if (WHOLE ? tok_ok : (tok_ok && tid + i * tpt < nblk)) {
                 const u32x4* p = &x[src[i] + static_cast<size_t>(t) * shard8];
                 a = load_nt(p);
                 c = load_nt(p + 1);
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
                     w1 |= e2m1_code(bf16_hi(yp[q + 4]) * outs) << (8 * q + 4);
                 }
             }
-            if (WHOLE || (tok_ok && b < nblk)) {
+            if (WHOLE ? tok_ok : (tok_ok && b < nblk)) {
                 packed[static_cast<size_t>(t) * nblk + b] = make_uint2(w0, w1);
                 scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf);
             }
@@ -168,16 +172,16 @@ inline BlockGeom block_geom(int H) {
     return g;
 }
 
-template <int BPT, bool WHOLE>
+template <int BPT, int TPT>
 int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
                       const float* global_scale, int T, int H, int shard, const BlockGeom& geo,
                       uint8_t* packed, uint8_t* scales, void* stream) {
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
     // as many blocks as fit on the GPU at once; each loops over its tokens
-    const int cap = device_cu_count() * resident_blocks(norm_quant_kernel<BPT, WHOLE>, kRowBlock, 0);
+    const int cap = device_cu_count() * resident_blocks(norm_quant_kernel<BPT, TPT>, kRowBlock, 0);
     const int grid = needed < cap ? needed : cap;
-    return launch(norm_quant_kernel<BPT, WHOLE>, dim3(grid), dim3(kRowBlock), 0, stream,
+    return launch(norm_quant_kernel<BPT, TPT>, dim3(grid), dim3(kRowBlock), 0, stream,
                   reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
                   shard / 8, geo.tpt, reinterpret_cast<uint2*>(packed), scales);
 }
@@ -197,16 +201,21 @@ extern "C" int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, con
     if (!x || !norm_w || !global_scale || !packed || !scales) return MOE_ERR_NULL_ARG;
     if (!all_aligned16(x, norm_w, packed, scales)) return MOE_ERR_ALIGN;
     const BlockGeom geo = block_geom(H);
-    const bool whole = geo.tpt == kRowBlock && H / 16 == geo.bpt * kRowBlock;
-#define MOE_NQ(B, W) launch_norm_quant<B, W>(x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream)
+    const int tpt_whole =
+        (geo.tpt == kRowBlock || geo.tpt == kWave) && H / 16 == geo.bpt * geo.tpt ? geo.tpt : 0;
+#define MOE_NQ_ARGS x, norm_w, gain_center, eps, global_scale, T, H, shard, geo, packed, scales, stream
+#define MOE_NQ(B) (tpt_whole == kRowBlock ? launch_norm_quant<B, kRowBlock>(MOE_NQ_ARGS) \
+                   : tpt_whole == kWave   ? launch_norm_quant<B, kWave>(MOE_NQ_ARGS)     \
+                                          : launch_norm_quant<B, 0>(MOE_NQ_ARGS))
     switch (geo.bpt) {
-        case 1: return whole ? MOE_NQ(1, true) : MOE_NQ(1, false);
-        case 2: return whole ? MOE_NQ(2, true) : MOE_NQ(2, false);
-        case 3: return whole ? MOE_NQ(3, true) : MOE_NQ(3, false);
-        case 4: return whole ? MOE_NQ(4, true) : MOE_NQ(4, false);
+        case 1: return MOE_NQ(1);
+        case 2: return MOE_NQ(2);
+        case 3: return MOE_NQ(3);
+        case 4: return MOE_NQ(4);
         default: return MOE_ERR_BAD_SHAPE;
     }
 #undef MOE_NQ
+#undef MOE_NQ_ARGS
 }
 
 extern "C" int moe_norm_quant_nvfp4(const uint16_t* x, const float* norm_w, float gain_center,
