@@ -9,7 +9,8 @@ inputs resident in HBM and every output and workspace allocated before the
 timed region. The default workload is the 8192-token prefill batch (H=8192,
 E=256, k=8, 5% invalid tokens). Prints one JSON line.
 
-Schedules (the headline is the default, overlap launched eagerly):
+Schedules (the headline is the default `auto`: overlap launched eagerly from
+2048 tokens, serial below):
   serial         the four calls in order on one stream
   overlap        route on the main stream, then norm + quant forked onto a
                  second stream beside dispatch -> combine (it depends on none
@@ -17,10 +18,11 @@ Schedules (the headline is the default, overlap launched eagerly):
                  ends when both are done
   overlap-route  norm + quant forked beside the route instead; the projection
                  is power-bound, so the two mostly slow each other down
-  graph          the overlap step captured once in a HIP graph and replayed;
-                 every kernel still runs every step. On this stack the replay
-                 runs the forked branch serially and is slower than the eager
-                 overlap, so it is reported, not used
+  graph          the overlap step (and, reported beside it, the serial step)
+                 captured once in a HIP graph and replayed; every kernel still
+                 runs every step. At the prefill shape the replay is slower
+                 than the eager overlap; at decode sizes, where launches
+                 dominate, the serial graph is the fastest schedule
 
 Alongside the throughput the line carries:
   stages        per-call mean duration (HIP events on the launch stream, from
@@ -166,9 +168,11 @@ def main():
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
                     help="skip the 1 GiB device-copy reference bandwidth")
-    ap.add_argument("--schedule", choices=["overlap", "overlap-route", "serial"], default="overlap",
+    ap.add_argument("--schedule", choices=["auto", "overlap", "overlap-route", "serial"], default="auto",
                     help="headline schedule: norm+quant on a second stream beside dispatch + combine "
-                         "(overlap) or beside the route (overlap-route), or all on one stream (serial)")
+                         "(overlap) or beside the route (overlap-route), or all on one stream (serial); "
+                         "auto = overlap from 2048 tokens, serial below (the streams' fork and join "
+                         "cost more than they save on small batches)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline schedule from a HIP graph instead of launching it eagerly")
     ap.add_argument("--no-fc1", dest="fc1", action="store_false",
@@ -281,6 +285,8 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1000.0 / steps
 
+    if args.schedule == "auto":
+        args.schedule = "overlap" if T >= 2048 else "serial"
     head_step = {"overlap": step_overlap, "overlap-route": step_overlap_route, "serial": step_serial}[args.schedule]
     # warm up eagerly on a side stream (as graph capture requires), then capture
     side = torch.cuda.Stream(device=dev)
@@ -308,26 +314,31 @@ def main():
                  "serial": "serial"}[args.schedule] + \
         (", HIP graph replay" if args.graph else ", eager launches")
 
-    # serial eager pass with per-call events on the launch stream
+    # serial eager pass with per-call events on the launch stream (stage times)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step_serial(events[i])
     torch.cuda.synchronize()
-    serial_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    serial_ms = timed(step_serial, args.steps)
     overlap_eager_ms = timed(step_overlap, args.steps)
     overlap_route_ms = timed(step_overlap_route, args.steps)
-    if args.graph and args.schedule == "overlap":
-        overlap_graph_ms = ms_per_step
-    else:
+
+    def graph_ms(step):
         g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            step()                       # warm the side stream the capture runs on
+        stream.wait_stream(side)
         with torch.cuda.graph(g2):
-            step_overlap()
+            step()
         torch.cuda.synchronize()
         g2.replay()
-        overlap_graph_ms = timed(g2.replay, args.steps)
+        ms = timed(g2.replay, args.steps)
         del g2
+        return ms
+
+    overlap_graph_ms = ms_per_step if args.graph and args.schedule == "overlap" else graph_ms(step_overlap)
+    serial_graph_ms = ms_per_step if args.graph and args.schedule == "serial" else graph_ms(step_serial)
 
     # cold: flush the 256 MB last-level cache (a 512 MiB write) before each step
     cold_ms = None
@@ -429,6 +440,7 @@ def main():
                       "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),
                       "overlap_graph_ms": round(overlap_graph_ms, 4),
+                      "serial_graph_ms": round(serial_graph_ms, 4),
                       "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4)},
         "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),
