@@ -30,11 +30,10 @@
 //    kernel (exclusive prefix of ceil(rows / 256) over experts, and one
 //    16-byte record per tile: expert, first row, row end), so a GEMM block
 //    learns its tile from one load; the grid is an upper bound, blocks past
-//    the last tile leave at once. Blocks are
-//    remapped so that each XCD walks a contiguous run of (row tile, column
-//    tile) with the column tile fastest: the blocks of one gathered A tile
-//    run side by side and find it in their XCD's L2, and so do an expert's
-//    weights across its row tiles.
+//    the last tile leave at once. Blocks are remapped so that each XCD
+//    walks a contiguous run of (row tile, column tile) with the column tile
+//    fastest: the blocks of one gathered A tile run side by side and find it
+//    in their XCD's L2, and so do an expert's weights across its row tiles.
 //  * Epilogue straight from the accumulators: the MFMAs take the weight
 //    rows as their first operand, so each lane holds 16 output columns of
 //    one grouped row, half of two 16-column blocks; the two lanes holding a
