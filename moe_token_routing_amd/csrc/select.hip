@@ -110,8 +110,11 @@ __device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, 
 }
 
 // Experts e = EPL*lane + i (i < EPL) live in lane e / EPL, so each lane reads
-// its logits (or split partials) as one contiguous run.
-template <int EPL>
+// its logits (or split partials) as one contiguous run. BATCH split partials
+// are loaded before any of them is added: 8 keep the registers of many waves
+// per SIMD (large batches split K 8 ways); 32 cut the dependent rounds of
+// loads when a small batch split K many ways (64 at 128 tokens).
+template <int EPL, int BATCH>
 __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
@@ -135,10 +138,10 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
             // a batch of splits is loaded before any is added (the loads
             // overlap); the sum still runs over the splits in order
 #pragma unroll 1
-            for (int p0 = 1; p0 < nsplit; p0 += kSplitBatch) {
-                float q[kSplitBatch][EPL];
+            for (int p0 = 1; p0 < nsplit; p0 += BATCH) {
+                float q[BATCH][EPL];
 #pragma unroll
-                for (int u = 0; u < kSplitBatch; ++u) {
+                for (int u = 0; u < BATCH; ++u) {
                     if (p0 + u < nsplit) {
                         load_run<EPL>(partials + (p0 + u) * plane + row, vec, n, q[u]);
                     } else {
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < kSplitBatch; ++u)
+                for (int u = 0; u < BATCH; ++u)
                     if (p0 + u < nsplit) {
 #pragma unroll
                         for (int i = 0; i < EPL; ++i) lg[i] += q[u][i];
@@ -273,7 +276,11 @@ template <int EPL>
 int launch_select_reg(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
                       const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
                       void* stream) {
-    return launch(select_reg_kernel<EPL>, dim3(ceil_div(T, kSelectWaves)), dim3(kSelectBlock), 0,
+    if (nsplit > 2 * kSplitBatch)
+        return launch(select_reg_kernel<EPL, 4 * kSplitBatch>, dim3(ceil_div(T, kSelectWaves)),
+                      dim3(kSelectBlock), 0, stream, partials, nsplit, scale, logits_in, bias, mask, T, E,
+                      k, logits, ids, w);
+    return launch(select_reg_kernel<EPL, kSplitBatch>, dim3(ceil_div(T, kSelectWaves)), dim3(kSelectBlock), 0,
                   stream, partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w);
 }
 
