@@ -103,9 +103,10 @@ def test_combine_edge_cases():
     np.testing.assert_array_equal(host(out), ref)
 
 
-@pytest.mark.parametrize("H", [8, 24, 256, 1032, 4104, 16384])
+@pytest.mark.parametrize("H", [8, 24, 256, 768, 1000, 1024, 1032, 4104, 16384])
 def test_combine_widths(H):
-    """Widths off the power-of-two grid, up to the maximum."""
+    """Widths off the power-of-two grid, up to the maximum; 768 and 1000 take
+    one wave per token with bounds checks, 1024 one wave per token without."""
     g = np.random.default_rng(H)
     T, k = 37, 5
     R = T * k + 9

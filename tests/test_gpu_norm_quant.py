@@ -84,7 +84,7 @@ def test_norm_quant_power_of_two_rows_exact():
         np.testing.assert_array_equal(p, rp)
 
 
-@pytest.mark.parametrize("H", [16, 48, 272, 2064, 16384])
+@pytest.mark.parametrize("H", [16, 48, 272, 1024, 2064, 4096, 16384])
 def test_norm_quant_widths(H):
     g = np.random.default_rng(H + 1)
     T = 29
