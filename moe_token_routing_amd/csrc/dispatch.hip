@@ -33,7 +33,9 @@ constexpr int kDispBlock = 256;
 constexpr int kDispWaves = kDispBlock / kWave;
 constexpr int kMaxTiles = 256;
 constexpr long long kFuseLimit = 1ll << 22;   // tiles * tiles * E read by the fused place step
-constexpr int kHistBatch = 8;                 // tile histograms loaded before they are added
+constexpr int kHistBatch = 32;                // tile histograms loaded before they are added
+constexpr int kIdBatch = 16;                  // ids per thread loaded before they are counted
+constexpr int kIdChunks = 16;                 // 64-slot chunks of a wave's quarter held in registers
 
 struct TilePlan {
     int n;        // slots
@@ -69,9 +71,18 @@ __global__ __launch_bounds__(kDispBlock) void hist_kernel(const int32_t* __restr
     for (int e = threadIdx.x; e < E; e += kDispBlock) lds[e] = 0;
     __syncthreads();
     const int base = blockIdx.x * tile;
-    for (int i = threadIdx.x; i < tile; i += kDispBlock) {
-        const int id = slot_id(ids, base + i, n, E);
-        if (id >= 0) atomicAdd(&lds[id], 1);
+    // kIdBatch ids per thread are loaded before any is counted, so a tile of
+    // up to kIdBatch * kDispBlock slots costs one memory round trip
+    for (int i0 = threadIdx.x; i0 < tile; i0 += kIdBatch * kDispBlock) {
+        int id[kIdBatch];
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u) {
+            const int i = i0 + u * kDispBlock;
+            id[u] = i < tile ? slot_id(ids, base + i, n, E) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u)
+            if (id[u] >= 0) atomicAdd(&lds[id[u]], 1);
     }
     __syncthreads();
     int32_t* row = tile_counts + static_cast<size_t>(blockIdx.x) * E;
@@ -109,6 +120,32 @@ __global__ __launch_bounds__(kDispBlock) void scan_kernel(int32_t* __restrict__ 
     }
 }
 
+// Ranks one 64-slot chunk (lane = slot f within the chunk) among the chunk's
+// slots with the same id and places it: equal ids are matched with ballots
+// over the id bits, so the rank is the number of earlier slots with that id.
+// run[id] holds the next free position of the wave's run of expert id.
+__device__ __forceinline__ void place_chunk(int id, int f, int n, int E, int idbits,
+                                            int32_t* run, int32_t* __restrict__ perm,
+                                            int32_t* __restrict__ dest) {
+    const int key = id >= 0 ? id : E;   // ids < E, and E itself marks "no entry"
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < idbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    if (id >= 0) {
+        const int rank = __popcll(peers & lanemask_lt());
+        const int pos = run[id] + rank;
+        perm[pos] = f;
+        dest[f] = pos;
+        // the last peer lane advances the running position of this id
+        if ((peers >> __lane_id()) == 1ull) run[id] = pos + 1;
+    } else if (f < n) {
+        dest[f] = -1;
+    }
+}
+
 // LDS layout: off[E + 1], hist[kDispWaves][E], then (FUSED) cnt[E], rel[E].
 // FUSED: tile_hist holds the raw tile histograms; the block derives the
 // expert totals (block 0 writes them to counts) and its exclusive prefix
@@ -126,6 +163,20 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     const int tid = threadIdx.x;
     const int lane = __lane_id();
     const int wave = tid / kWave;
+    // The wave's quarter of the tile, in 64-slot chunks. Up to kIdChunks
+    // chunks are loaded into registers here, before the tile sums, so their
+    // latency overlaps; steps (2) and (4) then read no ids from memory.
+    const int base = blockIdx.x * tile;
+    const int quarter = tile / kDispWaves;          // multiple of 64
+    const int q0 = base + wave * quarter;
+    const int nchunks = quarter / kWave;
+    const bool cached = nchunks <= kIdChunks;
+    int idr[kIdChunks];
+    if (cached) {
+#pragma unroll
+        for (int c = 0; c < kIdChunks; ++c)
+            idr[c] = c < nchunks ? slot_id(ids, q0 + c * kWave + lane, n, E) : -1;
+    }
     const int32_t* cnt = counts;
     const int32_t* rel = tile_hist + static_cast<size_t>(blockIdx.x) * E;
     if (FUSED) {
@@ -182,13 +233,16 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
         for (int e = tid; e <= E; e += kDispBlock) offsets[e] = off[e];
 
     // (2) per-wave histograms of the tile's quarters.
-    const int base = blockIdx.x * tile;
-    const int quarter = tile / kDispWaves;          // multiple of 64
-    const int q0 = base + wave * quarter;
     int32_t* my = hist + wave * E;
-    for (int i = lane; i < quarter; i += kWave) {
-        const int id = slot_id(ids, q0 + i, n, E);
-        if (id >= 0) atomicAdd(&my[id], 1);
+    if (cached) {
+#pragma unroll
+        for (int c = 0; c < kIdChunks; ++c)
+            if (idr[c] >= 0) atomicAdd(&my[idr[c]], 1);
+    } else {
+        for (int i = lane; i < quarter; i += kWave) {
+            const int id = slot_id(ids, q0 + i, n, E);
+            if (id >= 0) atomicAdd(&my[id], 1);
+        }
     }
     __syncthreads();
     // (3) starting position of each wave's run of each expert.
@@ -203,26 +257,15 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     }
     __syncthreads();
     // (4) rank and place, 64 slots at a time, in slot order within each wave.
-    const int idbits = 32 - __clz(E);   // ids < E, and E itself marks "no entry"
-    for (int i0 = 0; i0 < quarter; i0 += kWave) {
-        const int f = q0 + i0 + lane;
-        const int id = slot_id(ids, f, n, E);
-        const int key = id >= 0 ? id : E;
-        uint64_t peers = ~0ull;
-        for (int b = 0; b < idbits; ++b) {
-            const bool bit = (key >> b) & 1;
-            const uint64_t m = ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        if (id >= 0) {
-            const int rank = __popcll(peers & lanemask_lt());
-            const int pos = my[id] + rank;
-            perm[pos] = f;
-            dest[f] = pos;
-            // the last peer lane advances the running position of this id
-            if ((peers >> lane) == 1ull) my[id] = pos + 1;
-        } else if (f < n) {
-            dest[f] = -1;
+    const int idbits = 32 - __clz(E);
+    if (cached) {
+#pragma unroll
+        for (int c = 0; c < kIdChunks; ++c)
+            if (c < nchunks) place_chunk(idr[c], q0 + c * kWave + lane, n, E, idbits, my, perm, dest);
+    } else {
+        for (int i0 = 0; i0 < quarter; i0 += kWave) {
+            const int f = q0 + i0 + lane;
+            place_chunk(slot_id(ids, f, n, E), f, n, E, idbits, my, perm, dest);
         }
     }
     // (5) positions past the last valid entry hold -1; each tile clears its own range.
