@@ -26,6 +26,7 @@ from .nvfp4 import (gain_f32, rmsnorm_exact, rmsnorm_bf16, nvfp4_quantize,
                     norm_quant_nvfp4, global_scale, midpoint_boundary_blocks, dequantize,
                     rank_block_rows, norm_quant_nvfp4_rank_block)
 from .combine import combine
-from .fc1 import relu2, fc1_exact, expert_fc1_nvfp4, fc1_boundary_blocks
+from .fc1 import (relu2, silu, swiglu, SILU_ARGMIN, fc1_exact, expert_fc1_nvfp4, fc1_boundary_blocks,
+                  expert_fc1_swiglu_nvfp4, fc1_swiglu_boundary_blocks, swiglu_boundary_from_values)
 
 __all__ = [n for n in dir() if not n.startswith("_")]
