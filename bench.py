@@ -36,6 +36,8 @@ Alongside the throughput the line carries:
                 source (null otherwise)
   expert_fc1    the expert FC1 (moe_expert_fc1_nvfp4) at the FC1 workload of
                 the act-fusion GEMM page, against the FP16 MFMA peak
+  expert_fc1_swiglu  the SwiGLU form (moe_expert_fc1_swiglu_nvfp4) over the
+                same 2688 weight rows as gate and up halves
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -117,15 +119,18 @@ def cpu_baseline(w, sample_tokens: int):
             "sample": "first %d tokens of the %s workload as one batch, all four steps, %.1f s" % (S, w.name, dt)}
 
 
-def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10):
+def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10, swiglu: bool = False):
     """The expert FC1 on the dispatched NVFP4 input at the FC1 workload the
     act-fusion GEMM page times (K 1024, N 2688, 512 experts, top-22, 32768
     tokens): synthetic NVFP4 bytes, the path's own dispatch of synthetic
-    top-22 ids, HIP events around each call."""
+    top-22 ids, HIP events around each call. swiglu: the same 2688 weight
+    rows as gate and up halves (1344 output columns)."""
     w = wl.WORKLOADS["wide_k"]
-    T, k, E, K, N = w.T, w.k, w.E, w.H, wl.FC1_N["wide_k"]
+    T, k, E, K = w.T, w.k, w.E, w.H
+    N = wl.FC1_SWIGLU_N["wide_k"] if swiglu else wl.FC1_N["wide_k"]
+    rows = 2 * N if swiglu else N
     xp, xs = wl.fc1_activations(w, T, K)
-    wp, ws, gw = wl.fc1_weights(w, N, E, K)
+    wp, ws, gw = wl.fc1_weights(w, rows, E, K)
     ids = torch.from_numpy(wl.synthetic_topk_ids(w, T)).to(dev)
     X, XS = torch.from_numpy(xp).to(dev), torch.from_numpy(xs).to(dev)
     Wp, Ws, GW = torch.from_numpy(wp).to(dev), torch.from_numpy(ws).to(dev), torch.from_numpy(gw).to(dev)
@@ -136,9 +141,10 @@ def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10):
     yp = torch.empty((T * k, N // 2), dtype=torch.uint8, device=dev)
     ys = torch.empty((T * k, N // 16), dtype=torch.uint8, device=dev)
     wsp = torch.empty(m.expert_fc1_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
+    fn = m.expert_fc1_swiglu_nvfp4 if swiglu else m.expert_fc1_nvfp4
 
     def call():
-        m.expert_fc1_nvfp4(X, XS, gx, perm, offsets, k, Wp, Ws, GW, gy, y_packed=yp, y_scales=ys, workspace=wsp)
+        fn(X, XS, gx, perm, offsets, k, Wp, Ws, GW, gy, y_packed=yp, y_scales=ys, workspace=wsp)
 
     for _ in range(2):
         call()
@@ -149,12 +155,13 @@ def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10):
         b.record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    flop = 2.0 * T * k * N * K
+    flop = 2.0 * T * k * rows * K
     tf = flop / (ms * 1e-3) / 1e12
-    return {"workload": "K 1024, N 2688, 512 experts, top-22, 32768 tokens (720896 routed rows)",
+    what = ("SwiGLU, 1344 output columns over 2688 gate and up rows" if swiglu else "Relu2, N 2688")
+    return {"workload": "K 1024, %s, 512 experts, top-22, 32768 tokens (720896 routed rows)" % what,
             "ms": round(ms, 3), "TFLOPs": round(tf, 1), "unit_peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
             "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-            "bytes_in": int(T * K * 9 // 16 + E * N * K * 9 // 16), "bytes_out": int(T * k * N * 9 // 16)}
+            "bytes_in": int(T * K * 9 // 16 + E * rows * K * 9 // 16), "bytes_out": int(T * k * N * 9 // 16)}
 
 
 def main():
@@ -375,9 +382,10 @@ def main():
         rank_block = {"tp": tp, "ms": round(rb_ms, 4), "same_bytes_as_contiguous": same}
         del pooled, rb_packed, rb_scales
 
-    fc1 = None
+    fc1 = fc1_swiglu = None
     if args.fc1:
         fc1 = time_expert_fc1(m, wl, torch, dev, stream)
+        fc1_swiglu = time_expert_fc1(m, wl, torch, dev, stream, swiglu=True)
 
     names = ["route", "dispatch", "norm_quant", "combine"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
@@ -436,6 +444,7 @@ def main():
         "valid_tokens_per_s": round(int(mask_np.sum()) / (ms_per_step * 1e-3), 1),
         "stages": stages,
         "expert_fc1": fc1,
+        "expert_fc1_swiglu": fc1_swiglu,
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
                       "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),

@@ -22,6 +22,9 @@
  *
  *   moe_expert_fc1_nvfp4  gather grouped GEMM of the NVFP4 input with NVFP4
  *                         per-expert weights, Relu2, NVFP4 output
+ *   moe_expert_fc1_swiglu_nvfp4
+ *                         the same GEMM over gate and up weight rows, SwiGLU,
+ *                         NVFP4 output
  *
  * Conventions shared by every call:
  *   - Every array argument is a DEVICE pointer (memory the caller allocated on
@@ -280,6 +283,38 @@ int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales, const
                          const float* y_gs, int K, int N, int E,
                          uint8_t* y_packed, uint8_t* y_scales,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_expert_fc1_swiglu_nvfp4 — the expert FC1 with SwiGLU instead of Relu2.
+ *
+ * Defined by the same TensorRT-LLM PR #21842 description, which names SwiGLU
+ * as the gather grouped GEMM's other fused activation without giving its
+ * weight layout. The layout taken here: each expert's weights hold 2N rows,
+ * the gate projection's N rows first, then the up projection's N rows.
+ *
+ * For grouped position p < offsets[E] (expert e, token t as in
+ * moe_expert_fc1_nvfp4) and output column n < N:
+ *   g = sum_i xv(t,i) * wv(e,n,i),   u = sum_i xv(t,i) * wv(e,N+n,i)
+ *   y[p,n] = silu(g) * u,  silu(g) = g / (1 + exp(-g))   (FP32 evaluation)
+ * y is quantised per 16 consecutive n with the static scale y_gs exactly as
+ * moe_norm_quant_nvfp4 quantises its rows; positions p >= offsets[E] get zero
+ * codes and zero scales.
+ *
+ *   w_packed [E, 2N, K/2] u8, w_scales [E, 2N, K/16] u8: gate rows 0..N-1,
+ *            up rows N..2N-1 of each expert; w_gs [E] FP32 (device).
+ *   y_packed [T*k, N/2] u8, y_scales [T*k, N/16] u8: outputs, rows in
+ *            grouped (perm) order.
+ *   Every other argument, the ranges of T, k, E and K, the alignments and
+ *   the workspace are those of moe_expert_fc1_nvfp4 (the same
+ *   moe_expert_fc1_workspace_bytes); N >= 64 with N % 64 == 0.
+ * Errors: NULL_ARG, BAD_SHAPE, ALIGN, WORKSPACE, HIP.
+ */
+int moe_expert_fc1_swiglu_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_gs,
+                                const int32_t* perm, const int32_t* offsets, int T, int k,
+                                const uint8_t* w_packed, const uint8_t* w_scales, const float* w_gs,
+                                const float* y_gs, int K, int N, int E,
+                                uint8_t* y_packed, uint8_t* y_scales,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

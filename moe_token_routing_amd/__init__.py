@@ -45,6 +45,8 @@ _SIGNATURES = {
     "moe_expert_fc1_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_expert_fc1_nvfp4": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp,
                                       _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "moe_expert_fc1_swiglu_nvfp4": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                             _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -274,15 +276,35 @@ def expert_fc1_nvfp4(x_packed: torch.Tensor, x_scales: torch.Tensor, x_gs: torch
     w_packed [E,N,K/2] / w_scales [E,N,K/16] uint8, w_gs [E] fp32, x_gs and
     y_gs one-element fp32 GPU tensors. Returns (y_packed [T*k,N/2],
     y_scales [T*k,N/16]) uint8 in grouped order."""
+    return _expert_fc1("moe_expert_fc1_nvfp4", 1, x_packed, x_scales, x_gs, perm, offsets, k, w_packed,
+                       w_scales, w_gs, y_gs, y_packed, y_scales, workspace)
+
+
+def expert_fc1_swiglu_nvfp4(x_packed: torch.Tensor, x_scales: torch.Tensor, x_gs: torch.Tensor,
+                            perm: torch.Tensor, offsets: torch.Tensor, k: int,
+                            w_packed: torch.Tensor, w_scales: torch.Tensor, w_gs: torch.Tensor,
+                            y_gs: torch.Tensor, *, y_packed=None, y_scales=None, workspace=None):
+    """moe_expert_fc1_swiglu_nvfp4. As expert_fc1_nvfp4 with w_packed
+    [E,2N,K/2] / w_scales [E,2N,K/16] (gate rows, then up rows). Returns
+    (y_packed [T*k,N/2], y_scales [T*k,N/16]) uint8 in grouped order."""
+    return _expert_fc1("moe_expert_fc1_swiglu_nvfp4", 2, x_packed, x_scales, x_gs, perm, offsets, k, w_packed,
+                       w_scales, w_gs, y_gs, y_packed, y_scales, workspace)
+
+
+def _expert_fc1(fn, rows_per_col, x_packed, x_scales, x_gs, perm, offsets, k, w_packed, w_scales, w_gs, y_gs,
+                y_packed, y_scales, workspace):
     dev = x_packed.device
     if x_packed.dim() != 2 or w_packed.dim() != 3:
-        raise ValueError("x_packed must be [T,K/2] and w_packed [E,N,K/2]")
+        raise ValueError("x_packed must be [T,K/2] and w_packed [E,rows,K/2]")
     T, K = x_packed.shape[0], x_packed.shape[1] * 2
-    E, N = w_packed.shape[0], w_packed.shape[1]
+    E, rows = w_packed.shape[0], w_packed.shape[1]
+    if rows % rows_per_col:
+        raise ValueError("w_packed must hold gate and up rows (an even count)")
+    N = rows // rows_per_col
     _need(x_packed, "x_packed", (torch.uint8,), (T, K // 2), dev)
     _need(x_scales, "x_scales", (torch.uint8,), (T, K // 16), dev)
-    _need(w_packed, "w_packed", (torch.uint8,), (E, N, K // 2), dev)
-    _need(w_scales, "w_scales", (torch.uint8,), (E, N, K // 16), dev)
+    _need(w_packed, "w_packed", (torch.uint8,), (E, rows, K // 2), dev)
+    _need(w_scales, "w_scales", (torch.uint8,), (E, rows, K // 16), dev)
     _need(w_gs, "w_gs", (torch.float32,), (E,), dev)
     _need(perm, "perm", (torch.int32,), (T * k,), dev)
     _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
@@ -298,7 +320,7 @@ def expert_fc1_nvfp4(x_packed: torch.Tensor, x_scales: torch.Tensor, x_gs: torch
     need = expert_fc1_workspace_bytes(T, int(k), E)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check("moe_expert_fc1_nvfp4", lib().moe_expert_fc1_nvfp4(
+    _check(fn, getattr(lib(), fn)(
         _ptr(x_packed), _ptr(x_scales), _ptr(x_gs), _ptr(perm), _ptr(offsets), T, int(k),
         _ptr(w_packed), _ptr(w_scales), _ptr(w_gs), _ptr(y_gs), K, N, E,
         _ptr(y_packed), _ptr(y_scales), _ptr(workspace), workspace.numel(), _stream(dev)))

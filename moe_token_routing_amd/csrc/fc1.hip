@@ -172,7 +172,30 @@ __device__ __forceinline__ f16x2_t scale_pair(uint32_t two) {
 // conflicts for both, yet the kernel ran 7% slower with it.
 __device__ __forceinline__ int chunk_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-template <int WM, int WN, int MT, int NT>
+// silu(g) = g / (1 + e^-g), through e = e^-|g| so that the exponential never
+// overflows: g / (1 + e) for g >= 0, g e / (1 + e) below. FP32 throughout,
+// with v_rcp_f32 (1 ulp) for 1 / (1 + e), in [1/2, 1]: a few ulp in all, as
+// the IEEE-rounded division was, and 4% faster over the whole kernel.
+__device__ __forceinline__ float silu(float g) {
+    const float e = expf(-fabsf(g));
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
+    return g >= 0.f ? g * r : (g * e) * r;
+}
+
+// SWIGLU: the weights hold 2 N_out rows, the gate projection's rows first,
+// then the up projection's. In a block's B tile, 32-row tile jt holds the
+// gate and up rows of the 16 output columns n0_out + 16 jt + j, j < 16, with
+// tile row rr = 8 (j >> 2) + 4 half + (j & 3) (half 0 gate, 1 up): the rows
+// one MFMA accumulator gives lanes 0-31 are the gate rows, those it gives
+// lanes 32-63 the up rows of the same columns, in the same register.
+__device__ __forceinline__ int swiglu_weight_row(int br, int n0_out, int n_out) {
+    const int jt = br >> 5, rr = br & 31;
+    const int half = (rr >> 2) & 1;
+    const int j = ((rr >> 3) << 2) | (rr & 3);
+    return half * n_out + n0_out + 16 * jt + j;
+}
+
+template <bool SWIGLU, int WM, int WN, int MT, int NT>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void fc1_gemm_kernel(
     const uint8_t* __restrict__ x_packed, const uint8_t* __restrict__ x_scales,
     const float* __restrict__ x_gs, const int32_t* __restrict__ perm, const int32_t* __restrict__ tile_start,
@@ -200,7 +223,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int nt = logical - mt * ntn;
     const int4 info = tile_info[mt];
     const int e = info.x, m0 = info.y, row_end = info.z;
-    const int n0 = nt * BN;
+    const int n0 = nt * BN;                         // first weight row (Relu2)
+    const int n_out = SWIGLU ? N / 2 : N;           // output columns
+    const int n0_out = SWIGLU ? nt * (BN / 2) : n0;
 
     // this thread's load assignment: row r of the A tile, K half h of a
     // stage; B row halves tid + i THREADS (i < NBI) of the 2 BN
@@ -222,7 +247,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
         b_ok[i] = idx < 2 * BN;
         b_r[i] = b_ok[i] ? idx >> 1 : 0;
         b_h[i] = idx & 1;
-        const size_t wrow = static_cast<size_t>(e) * N + n0 + b_r[i];
+        const int brow = SWIGLU ? swiglu_weight_row(b_r[i], n0_out, n_out) : n0 + b_r[i];
+        const size_t wrow = static_cast<size_t>(e) * N + brow;
         wb[i] = w_packed + wrow * kb + b_h[i] * 16;
         wsb[i] = w_scales + wrow * ks;
     }
@@ -377,18 +403,51 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 
     // Epilogue, from the accumulators (no LDS): the MFMAs ran with the weight
     // rows as the first operand, so lane l of accumulator (i, jn) holds
-    // grouped row (l & 31) of row tile i and output columns 8 (q >> 2) +
-    // 4 (l >> 5) + (q & 3), q < 16, of column tile jn. A 16-column block is
-    // then values q = 8 blk .. 8 blk + 7 of lanes l and l + 32, which meet
-    // through one v_permlane32_swap for the block maximum and one for the
-    // codes. y = Relu2(alpha acc), then the pre-expert quantiser's FP32 steps.
+    // grouped row (l & 31) of row tile i and weight rows 8 (q >> 2) +
+    // 4 (l >> 5) + (q & 3), q < 16, of column tile jn.
+    //  Relu2: a 16-column output block is values q = 8 blk .. 8 blk + 7 of
+    //  lanes l and l + 32, which meet through one v_permlane32_swap for the
+    //  block maximum and one for the codes.
+    //  SwiGLU: lane l < 32 holds the gate values of the tile's 16 columns,
+    //  lane l + 32 the up values (q = column); one swap per pair (q, q + 8)
+    //  gives the lower lane gate and up of columns 0-7, the upper lane those
+    //  of columns 8-15, so each lane encodes 8 codes of the block and writes
+    //  them itself, and only the block maximum crosses lanes.
+    // Then the pre-expert quantiser's FP32 steps.
     const float alpha = 1.0f / (*x_gs * w_gs[e]);
     const float gs = *y_gs;
     const float rcp_gs = 1.0f / gs;
     constexpr float kRcp6 = 1.0f / 6.0f;
-    const size_t yrow_b = static_cast<size_t>(N) / 2, yrow_s = static_cast<size_t>(N) / 16;
+    const size_t yrow_b = static_cast<size_t>(n_out) / 2, yrow_s = static_cast<size_t>(n_out) / 16;
     const int half = lane >> 5;
-    // lane pair (l, l + 32) -> the block's 8 code bytes: the lower lane
+    // E4M3 scale byte and the 8 codes of y under it (q = y out, -0 -> +0)
+    auto encode8 = [&](const float (&y)[8], float amax, uint32_t& sf, uint32_t& w) {
+        const float sc = gs * (amax * kRcp6);
+        sf = e4m3_scale_code(sc);
+        const float sf_f = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sf), 0);
+        const float d = sf_f * rcp_gs;
+        const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
+        w = 0;
+        if (amax < INFINITY && fabsf(outs) < INFINITY) {
+            // the hardware conversion with unit scale rounds finite values to
+            // nearest even and saturates
+            float q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) q[u] = __builtin_fmaf(y[u], outs, 0.0f);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w |= e2m1_code(y[u] * outs) << (4 * u);
+        }
+    };
+    auto pair_max = [](float lm) {
+        const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+        return fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));
+    };
+    // Relu2: lane pair (l, l + 32) -> the block's 8 code bytes: the lower lane
     // writes bytes 0-3 (its codes 0-3, the upper lane's 4-7), the upper lane
     // bytes 4-7 (its codes 12-15 after the lower lane's 8-11)
     const uint32_t sel = half ? 0x07060302u : 0x05040100u;
@@ -398,42 +457,47 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
         const bool row_ok = pr >= 0 && pr < row_end;
 #pragma unroll
         for (int jn = 0; jn < NT; ++jn) {
-            const int c0 = n0 + wn * 32 * NT + jn * 32;
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+            if constexpr (SWIGLU) {
+                const int c0 = n0_out + 16 * (wn * NT + jn);
                 float y[8];
+                float lm = 0.f;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const float v = alpha * acc[i][jn][8 * blk + u];
-                    const float rl = v > 0.f ? v : 0.f;
-                    y[u] = rl * rl;
+                    const auto gu = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][jn][u]),
+                                                                     __float_as_uint(acc[i][jn][8 + u]), false, false);
+                    const float g = alpha * __uint_as_float(gu[0]);
+                    const float v = alpha * __uint_as_float(gu[1]);
+                    y[u] = silu(g) * v;
+                    lm = fmaxf(lm, fabsf(y[u]));
                 }
-                float lm = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-                const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
-                const float amax = fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));   // y >= 0
-                const float sc = gs * (amax * kRcp6);
-                const uint32_t sf = e4m3_scale_code(sc);
-                const float sf_f = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sf), 0);
-                const float d = sf_f * rcp_gs;
-                const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
-                uint32_t w = 0;
-                if (amax < INFINITY && fabsf(outs) < INFINITY) {
-                    // y >= 0, so q = y * out is never -0; the hardware conversion
-                    // with unit scale rounds finite values to nearest even and saturates
-                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0] * outs, y[1] * outs, 1.0f, 0);
-                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * outs, y[3] * outs, 1.0f, 1);
-                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * outs, y[5] * outs, 1.0f, 2);
-                    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * outs, y[7] * outs, 1.0f, 3);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) w |= e2m1_code(y[u] * outs) << (4 * u);
-                }
-                const auto ws = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-                const uint32_t word = __builtin_amdgcn_perm(ws[1], ws[0], sel);
+                uint32_t sf, w;
+                encode8(y, pair_max(lm), sf, w);
                 if (row_ok) {
-                    const int cb = c0 + 16 * blk;
-                    *reinterpret_cast<uint32_t*>(y_packed + static_cast<size_t>(pr) * yrow_b + cb / 2 + 4 * half) = word;
-                    if (half == 0) y_scales[static_cast<size_t>(pr) * yrow_s + cb / 16] = static_cast<uint8_t>(sf);
+                    *reinterpret_cast<uint32_t*>(y_packed + static_cast<size_t>(pr) * yrow_b + c0 / 2 + 4 * half) = w;
+                    if (half == 0) y_scales[static_cast<size_t>(pr) * yrow_s + c0 / 16] = static_cast<uint8_t>(sf);
+                }
+            } else {
+                const int c0 = n0 + wn * 32 * NT + jn * 32;
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    float y[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float v = alpha * acc[i][jn][8 * blk + u];
+                        const float rl = v > 0.f ? v : 0.f;
+                        y[u] = rl * rl;
+                    }
+                    const float lm = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                                           fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+                    uint32_t sf, w;
+                    encode8(y, pair_max(lm), sf, w);                    // y >= 0
+                    const auto ws = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+                    const uint32_t word = __builtin_amdgcn_perm(ws[1], ws[0], sel);
+                    if (row_ok) {
+                        const int cb = c0 + 16 * blk;
+                        *reinterpret_cast<uint32_t*>(y_packed + static_cast<size_t>(pr) * yrow_b + cb / 2 + 4 * half) = word;
+                        if (half == 0) y_scales[static_cast<size_t>(pr) * yrow_s + cb / 16] = static_cast<uint8_t>(sf);
+                    }
                 }
             }
         }
@@ -445,7 +509,7 @@ constexpr int kFcMinBM = 256;
 
 // Lays out the row tiles of this configuration's height, then launches the
 // GEMM over them.
-template <int WM, int WN, int MT, int NT>
+template <bool SWIGLU, int WM, int WN, int MT, int NT>
 int launch_fc1(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_gs, const int32_t* perm,
                const int32_t* offsets, int32_t* tile_start, int4* tile_info, int k, const uint8_t* w_packed,
                const uint8_t* w_scales, const float* w_gs, const float* y_gs, int K, int N, int E,
@@ -459,7 +523,7 @@ int launch_fc1(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_
     const int rc = launch(fc1_tiles_kernel, dim3(1), dim3(kFcTilesBlock), 0, stream, offsets, E,
                           static_cast<int>(P), S::BM, static_cast<int>(m_upper), tile_start, tile_info);
     if (rc) return rc;
-    return launch(fc1_gemm_kernel<WM, WN, MT, NT>, dim3(static_cast<unsigned>(per_xcd * 8)), dim3(S::THREADS),
+    return launch(fc1_gemm_kernel<SWIGLU, WM, WN, MT, NT>, dim3(static_cast<unsigned>(per_xcd * 8)), dim3(S::THREADS),
                   S::LDS, stream, x_packed, x_scales, x_gs, perm, tile_start, tile_info, k, w_packed,
                   w_scales, w_gs, y_gs, K, N, E, static_cast<int>(P), static_cast<int>(m_upper),
                   y_packed, y_scales);
@@ -484,17 +548,19 @@ extern "C" size_t moe_expert_fc1_workspace_bytes(int T, int k, int E) {
     return fc1_tile_start_bytes(E) + static_cast<size_t>(fc1_row_tiles_upper(P, E, kFcMinBM)) * sizeof(int4);
 }
 
-extern "C" int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales,
-                                    const float* x_global_scale, const int32_t* perm,
-                                    const int32_t* offsets, int T, int k, const uint8_t* w_packed,
-                                    const uint8_t* w_scales, const float* w_global_scale,
-                                    const float* y_global_scale, int K, int N, int E,
-                                    uint8_t* y_packed, uint8_t* y_scales, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-    using namespace moe;
+namespace moe {
+namespace {
+// Shared argument checks, zero fill of the unrouted rows and launch. N is
+// the output width; the weights hold N rows (Relu2) or 2 N (SwiGLU).
+template <bool SWIGLU>
+int expert_fc1(const uint8_t* x_packed, const uint8_t* x_scales, const float* x_global_scale,
+               const int32_t* perm, const int32_t* offsets, int T, int k, const uint8_t* w_packed,
+               const uint8_t* w_scales, const float* w_global_scale, const float* y_global_scale, int K,
+               int N, int E, uint8_t* y_packed, uint8_t* y_scales, void* workspace,
+               size_t workspace_bytes, void* stream) {
     if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_BAD_SHAPE;
-    if (K < kFcKS || K > MOE_MAX_HIDDEN || K % kFcKS != 0 || N < 128 || N % 128 != 0 ||
-        N > 8 * MOE_MAX_HIDDEN)
+    const bool n_ok = SWIGLU ? (N >= 64 && N % 64 == 0) : (N >= 128 && N % 128 == 0);
+    if (K < kFcKS || K > MOE_MAX_HIDDEN || K % kFcKS != 0 || !n_ok || N > 8 * MOE_MAX_HIDDEN)
         return MOE_ERR_BAD_SHAPE;
     const long long P = static_cast<long long>(T) * k;
     if (P >= (1ll << 31)) return MOE_ERR_BAD_SHAPE;
@@ -517,11 +583,39 @@ extern "C" int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_sc
     const int rc = launch(fc1_fill_kernel, dim3(gf), dim3(256), 0, stream, offsets, E, static_cast<int>(P), N,
                 reinterpret_cast<u32x4*>(y_packed), reinterpret_cast<uint32_t*>(y_scales));
     if (rc) return rc;
-    // widest column tile that divides N: 192, 256 or 128 columns
+    // widest column tile that divides the weight rows: 192, 256 or 128 rows
+    // (96, 128 or 64 output columns under SwiGLU)
+    const int rows = SWIGLU ? 2 * N : N;
 #define FC1_ARGS x_packed, x_scales, x_global_scale, perm, offsets, tile_start, tile_info, k, w_packed, \
-                 w_scales, w_global_scale, y_global_scale, K, N, E, P, y_packed, y_scales, stream
-    if (N % 192 == 0) return launch_fc1<4, 2, 2, 3>(FC1_ARGS);
-    if (N % 256 == 0) return launch_fc1<2, 4, 4, 2>(FC1_ARGS);
-    return launch_fc1<4, 2, 2, 2>(FC1_ARGS);
+                 w_scales, w_global_scale, y_global_scale, K, rows, E, P, y_packed, y_scales, stream
+    if (rows % 192 == 0) return launch_fc1<SWIGLU, 4, 2, 2, 3>(FC1_ARGS);
+    if (rows % 256 == 0) return launch_fc1<SWIGLU, 2, 4, 4, 2>(FC1_ARGS);
+    return launch_fc1<SWIGLU, 4, 2, 2, 2>(FC1_ARGS);
 #undef FC1_ARGS
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_expert_fc1_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales,
+                                    const float* x_global_scale, const int32_t* perm,
+                                    const int32_t* offsets, int T, int k, const uint8_t* w_packed,
+                                    const uint8_t* w_scales, const float* w_global_scale,
+                                    const float* y_global_scale, int K, int N, int E,
+                                    uint8_t* y_packed, uint8_t* y_scales, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return moe::expert_fc1<false>(x_packed, x_scales, x_global_scale, perm, offsets, T, k, w_packed, w_scales,
+                                  w_global_scale, y_global_scale, K, N, E, y_packed, y_scales, workspace,
+                                  workspace_bytes, stream);
+}
+
+extern "C" int moe_expert_fc1_swiglu_nvfp4(const uint8_t* x_packed, const uint8_t* x_scales,
+                                           const float* x_global_scale, const int32_t* perm,
+                                           const int32_t* offsets, int T, int k, const uint8_t* w_packed,
+                                           const uint8_t* w_scales, const float* w_global_scale,
+                                           const float* y_global_scale, int K, int N, int E,
+                                           uint8_t* y_packed, uint8_t* y_scales, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+    return moe::expert_fc1<true>(x_packed, x_scales, x_global_scale, perm, offsets, T, k, w_packed, w_scales,
+                                 w_global_scale, y_global_scale, K, N, E, y_packed, y_scales, workspace,
+                                 workspace_bytes, stream);
 }

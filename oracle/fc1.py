@@ -196,8 +196,8 @@ def fc1_swiglu_boundary_blocks(x_packed, x_scales, gs_x, perm, offsets, k, w_pac
     The gate and up values carry the Relu2 evaluation's bound (FP32 sums of
     the exact products with at most `adds` roundings, then alpha). The FP32
     evaluation of silu(g) * u (an exponential within a few ulp, an addition,
-    a division and two products) is assumed within `rel` of the value it is
-    given, plus |u| * 2^-140 + 2^-148 where the exponential or the result is
+    a reciprocal within 1 ulp and up to three products) is assumed within
+    `rel` (16 ulp) of the value it is given, plus |u| * 2^-140 + 2^-148 where the exponential or the result is
     subnormal (an exact zero stays exact). y then lies between the smallest
     and largest silu(g) * u over the gate and up intervals, widened by that
     error. A block is flagged when

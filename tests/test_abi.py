@@ -30,7 +30,8 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) == {"moe_status_string", "moe_route_workspace_bytes", "moe_route",
                           "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_norm_quant_nvfp4",
                           "moe_norm_quant_nvfp4_rank_block", "moe_combine",
-                          "moe_expert_fc1_workspace_bytes", "moe_expert_fc1_nvfp4"}
+                          "moe_expert_fc1_workspace_bytes", "moe_expert_fc1_nvfp4",
+                          "moe_expert_fc1_swiglu_nvfp4"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(m._SIGNATURES)
@@ -143,3 +144,12 @@ def test_expert_fc1_rejects_before_launch(lib):
     assert f(*args(x=None)) == -1
     assert f(*args(ws_b=ws - 1)) == -4
     assert f(*args(T=0)) == 0
+    g = lib.moe_expert_fc1_swiglu_nvfp4   # N output columns over 2N weight rows
+    assert g(*args(N=96)) == -2        # N % 64
+    assert g(*args(N=0)) == -2
+    assert g(*args(K=96)) == -2
+    assert g(*args(x=None)) == -1
+    assert g(*args(ws_b=ws - 1)) == -4
+    assert g(*args(T=0)) == 0
+    assert g(*args(T=0, N=64)) == 0    # 64 columns: allowed here, not with Relu2
+    assert f(*args(T=0, N=64)) == -2

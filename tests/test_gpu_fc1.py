@@ -138,3 +138,101 @@ def test_fc1_full_workload_sampled():
     used = int(offsets[-1])
     assert used == T * k
     print("wide_k sampled rows %d: boundary blocks %d of %d, mismatches inside %d" % (len(rows), nset, near.size, nmis))
+
+
+# ---- SwiGLU --------------------------------------------------------------
+
+def _swiglu_values(acc):
+    N = acc.shape[1] // 2
+    return O.swiglu(acc[:, :N], acc[:, N:])
+
+
+def _run_swiglu(xp, xs, gx, perm, offsets, k, wp, ws, gw, gy, what):
+    require_gpu()
+    note("fc1 swiglu %s T=%d K=%d N=%d E=%d k=%d" % (what, xp.shape[0], xp.shape[1] * 2, wp.shape[1] // 2,
+                                                      wp.shape[0], k))
+    yp, ys = m.expert_fc1_swiglu_nvfp4(dev(xp), dev(xs), scalar_dev(gx), dev(perm), dev(offsets), k,
+                                       dev(wp), dev(ws), dev(gw), scalar_dev(gy))
+    torch.cuda.synchronize()
+    return host(yp), host(ys)
+
+
+def _case_swiglu(T, k, E, K, N, seed, invalid=0.0, skew=None):
+    g = np.random.default_rng(seed)
+    w = wl.WORKLOADS["wide_k"]
+    xp, xs = wl.fc1_activations(w, T, K)
+    wp, ws, gw = wl.fc1_weights(w, 2 * N, E, K)
+    perm, offsets = _routing(g, T, k, E, invalid, skew)
+    gx = np.float32(37.5)
+    acc, _ = O.fc1_exact(xp, xs, gx, perm, offsets, k, wp, ws, gw)
+    gy = O.global_scale(_swiglu_values(acc))
+    return xp, xs, gx, perm, offsets, k, wp, ws, gw, gy
+
+
+@pytest.mark.parametrize("T,k,E,K,N,invalid,skew", [
+    (37, 3, 5, 128, 64, 0.1, None),             # 128 weight rows per tile (64 columns), ragged, invalid slots
+    (300, 2, 4, 64, 128, 0.0, [10, 0, 1, 3]),   # 256-row tiles, an empty expert, one over several tiles
+    (64, 4, 16, 256, 192, 0.0, None),           # 192-row tiles (96 columns), many small experts
+    (40, 2, 3, 576, 320, 0.0, None),            # 128-row tiles over 640 rows, 9 K stages
+    (33, 3, 5, 1088, 384, 0.05, None),          # 17 K stages, a partial scale row
+])
+def test_fc1_swiglu_small(T, k, E, K, N, invalid, skew):
+    args = _case_swiglu(T, k, E, K, N, seed=T + E + 1, invalid=invalid, skew=skew)
+    xp, xs, gx, perm, offsets, k, wp, ws, gw, gy = args
+    got_p, got_s = _run_swiglu(*args, "small")
+    ref_p, ref_s = O.expert_fc1_swiglu_nvfp4(*args)
+    near = O.fc1_swiglu_boundary_blocks(*args)
+    nset, nmis = _check(got_p, got_s, ref_p, ref_s, near, "fc1 swiglu")
+    used = int(offsets[-1])
+    assert got_p.shape == (T * k, N // 2)
+    assert not got_p[used:].any() and not got_s[used:].any()
+    # the output's signs: negative codes appear (silu and up both change sign)
+    codes = unpack_codes(got_p[:used])
+    assert (codes & 8).any() and (codes[codes > 0] & 7).any()
+    print("boundary blocks %d of %d, code mismatches inside %d" % (nset, near.size, nmis))
+
+
+def test_fc1_swiglu_and_relu2_share_the_grouping():
+    """Same input, grouping and weight bytes: the SwiGLU call over 2N rows and
+    the Relu2 call over the same 2N rows both leave the rows past the routed
+    count zero and write every routed row."""
+    args = _case_swiglu(50, 2, 4, 128, 128, seed=77, invalid=0.2)
+    xp, xs, gx, perm, offsets, k, wp, ws, gw, gy = args
+    sp, ss = _run_swiglu(*args, "grouping")
+    rp, rs = _run(xp, xs, gx, perm, offsets, k, wp, ws, gw, gy, "grouping relu2")
+    used = int(offsets[-1])
+    assert used < len(perm)
+    for p_, s_ in ((sp, ss), (rp, rs)):
+        assert not p_[used:].any() and not s_[used:].any()
+        assert (s_[:used] != 0).any(axis=1).all()
+
+
+def test_fc1_swiglu_full_workload_sampled():
+    """T = 32768 tokens, top-22 of 512 experts, K 1024, 1344 output columns
+    over 2688 gate and up rows, at full size; rows of 6 experts checked
+    against the oracle."""
+    require_gpu()
+    w = wl.WORKLOADS["wide_k"]
+    T, k, E, K, N = w.T, w.k, w.E, w.H, wl.FC1_SWIGLU_N["wide_k"]
+    xp, xs = wl.fc1_activations(w, T, K)
+    wp, ws, gw = wl.fc1_weights(w, 2 * N, E, K)
+    ids = wl.synthetic_topk_ids(w, T)
+    counts, offsets, perm, dest = O.dispatch(ids, E)
+    perm, offsets = perm.astype(np.int32), offsets.astype(np.int32)
+    gx = np.float32(37.5)
+    g = np.random.default_rng(12)
+    experts = g.choice(E, size=6, replace=False)
+    rows = np.concatenate([np.arange(offsets[e], offsets[e + 1])[:24] for e in experts])
+    sub_ids = np.full((len(rows), 1), -1, dtype=np.int32)
+    sub_ids[:, 0] = np.array([np.searchsorted(offsets, r, side="right") - 1 for r in rows])
+    c2, off2, perm2, _ = O.dispatch(sub_ids, E)
+    tok = perm[rows] // k
+    sub_args = (xp[tok], xs[tok], gx, perm2.astype(np.int32), off2.astype(np.int32), 1, wp, ws, gw)
+    acc, _ = O.fc1_exact(*sub_args)
+    gy = O.global_scale(_swiglu_values(acc))
+    ref_p, ref_s = O.expert_fc1_swiglu_nvfp4(*sub_args, gy)
+    near = O.fc1_swiglu_boundary_blocks(*sub_args, gy)
+    got_p, got_s = _run_swiglu(xp, xs, gx, perm, offsets, k, wp, ws, gw, gy, "wide_k full")
+    nset, nmis = _check(got_p[rows[perm2]], got_s[rows[perm2]], ref_p, ref_s, near, "fc1 swiglu wide_k")
+    assert int(offsets[-1]) == T * k
+    print("wide_k sampled rows %d: boundary blocks %d of %d, mismatches inside %d" % (len(rows), nset, near.size, nmis))

@@ -90,6 +90,9 @@ _FIELDS = ["hidden", "W", "bias", "mask", "tie_logits", "expert_out", "slots",
 # Output features of the expert FC1 where a workload stands for the FC1 the
 # act-fusion GEMM page times (K 1024, N 2688, 512 experts, top-22).
 FC1_N = {"wide_k": 2688}
+# Output columns of the SwiGLU form of the same FC1: the 2688 weight rows
+# split into gate and up halves.
+FC1_SWIGLU_N = {"wide_k": 1344}
 
 
 def rng(workload: Workload, field: str) -> np.random.Generator:
