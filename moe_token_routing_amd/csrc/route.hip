@@ -11,20 +11,28 @@
 // Design (gfx950):
 //  * The projection is a dense contraction, so it runs on MFMA. FP32 weights
 //    are split exactly into three BF16 planes, W = W0 + W1 + W2 (each plane
-//    holds the next 8 significant bits of what the previous ones missed; for
-//    |W| >= 2^-100 the sum is exact). A BF16 input times a BF16 plane is exact
-//    in FP32, so the three MFMA products h*W0 + h*W1 + h*W2 accumulate exact
-//    products of the FP32 weights in FP32 (v_mfma_f32_32x32x16_bf16). An FP32
-//    input is split the same way and the six products with plane-index sum
-//    <= 2 are accumulated (the three dropped ones are below 2^-23 of |h*W|).
+//    holds the next 8 significant bits of what the previous ones missed, to
+//    nearest even; for |W| >= 2^-100 the sum is exact). A BF16 input times a
+//    BF16 plane is exact in FP32, so the three MFMA products h*W0 + h*W1 +
+//    h*W2 accumulate exact products of the FP32 weights in FP32
+//    (v_mfma_f32_32x32x16_bf16). An FP32 input is split the same way (by a
+//    kernel of its own, into planes in HBM) and the six products with
+//    plane-index sum <= 2 are accumulated (the three dropped ones are below
+//    2^-23 of |h*W|).
+//  * Where the weights are split depends on the token count: from 4096
+//    tokens one kernel per call writes the planes in MFMA fragment order and
+//    each wave loads its fragments with one 16-byte load each; below, each
+//    wave loads the FP32 weights themselves, 8 consecutive K values of one
+//    expert per lane (the B operand's layout), and splits them in registers
+//    (v_cvt_pk_bf16_f32, two values at a time), which saves the split
+//    kernel. Both give the same planes.
 //  * Block tile up to 128 tokens x 256 experts (all of them at E = 256, so the
 //    input is read from HBM once), four waves of up to 128 x 64. The input
 //    rows, shared by the four waves, go through a ring of LDS stages filled
-//    by direct-to-LDS loads; the weight planes are stored pre-split in MFMA
-//    fragment order and each wave loads its own fragments straight into
-//    registers. Split-K when the tile grid alone cannot fill the GPU, arranged
-//    so that each XCD reads one K-slice of the weight planes (which then
-//    stays in its L2). Partial sums go to the workspace.
+//    by direct-to-LDS loads; the weights go straight to registers, one K-step
+//    ahead. Split-K when the tile grid alone cannot fill the GPU, arranged so
+//    that each XCD reads one K-slice of the weights (which then stays in its
+//    L2). Partial sums go to the workspace.
 //  * The selection (select.hip) adds the split-K partials in a fixed order,
 //    applies the scale and picks the top k.
 #include <cmath>
@@ -75,17 +83,13 @@ __device__ __forceinline__ int slot_bytes(int row, int c) { return (row * 2 + (c
 // [16 s + 8 (l >> 5), +8) of expert 32 (G j + g) + (l & 31) -- exactly the
 // B operand of v_mfma_f32_32x32x16_bf16 for those 32 experts, so one wave
 // loads a fragment with one 16-byte load per lane. Experts beyond E are zero.
-// Block 0 also clears the 256-byte zero block the projection reads in place
-// of out-of-range input.
 //
 // One thread per fragment lane and K-step: it reads its 8 FP32 weights once
 // (32 bytes) and writes their three planes, so each wave writes three 1 KB
 // runs.
 __global__ __launch_bounds__(256) void split_weight_kernel(const float* __restrict__ W, int E, int H,
                                                            int G, int tiles_n,
-                                                           u32x4* __restrict__ frags,
-                                                           uint32_t* __restrict__ zero_block) {
-    if (blockIdx.x == 0 && threadIdx.x < 64) zero_block[threadIdx.x] = 0u;
+                                                           u32x4* __restrict__ frags) {
     const int nks = H / 16;
     const int per_step = G * 64;                       // (group, lane) pairs of one plane
     const long long total = static_cast<long long>(tiles_n) * nks * per_step;
@@ -128,9 +132,10 @@ __global__ __launch_bounds__(256) void split_weight_kernel(const float* __restri
 // input goes through LDS: a ring of DA stages filled DA-1 steps ahead by
 // direct-to-LDS 16-byte loads (global_load_lds_dwordx4: lane l writes bytes
 // [16 l, 16 l + 16) of the instruction's 1 KB LDS window). Each wave loads its
-// own weight fragments straight into registers one step ahead (two register
-// sets), which keeps the weight traffic out of LDS. Two blocks share a CU, so
-// one block's waits overlap the other's MFMAs.
+// own weights (fragments, or FP32 values it splits at the step) straight
+// into registers one step ahead (two register sets), which keeps the weight
+// traffic out of LDS. Two blocks share a CU, so one block's
+// waits overlap the other's MFMAs.
 //
 // LDS stage layout: rows of 16 BF16 (two 16-byte chunks), NA planes x BM
 // rows. Chunk c of row R sits in slot 2 R + (c ^ swz(R)),
@@ -145,7 +150,6 @@ template <int NA, int MT, int NT>
 struct GemmShape {
     static constexpr int BM = 32 * MT;
     static constexpr int BN = 128 * NT;
-    static constexpr int G = BN / 32;                    // weight fragments per plane and K-step
     static constexpr int A_ROWS = NA * BM;
     static constexpr int A_LOADS = A_ROWS * 2 / kWave;   // 1 KB load instructions per stage
     static constexpr int STAGE = A_ROWS * 32;            // bytes
@@ -153,31 +157,58 @@ struct GemmShape {
 };
 
 // Input rows [m0, m0 + BM) x K columns [k0, k0 + 16) of every input plane into
-// the stage buffer at `base`; rows beyond T read the zero block.
+// the stage buffer at `base`; rows beyond T read row T - 1 (their results
+// are never stored).
 template <typename S>
 __device__ __forceinline__ void issue_a(char* base, int k0, int wave, int lane, int m0, int T, int H,
-                                        const uint16_t* __restrict__ a_planes, size_t a_plane,
-                                        const uint16_t* __restrict__ zero16) {
+                                        const uint16_t* __restrict__ a_planes, size_t a_plane) {
     const int lr = lane >> 1;
     const int sc = lane & 1;
     for (int i = wave; i < S::A_LOADS; i += kGemmWaves) {
         const int R = i * 32 + lr;
         const int c = sc ^ swz(R);
         const int p = R / S::BM, r = R - p * S::BM;
-        const int row = m0 + r;
-        const uint16_t* src = row < T ? a_planes + p * a_plane + static_cast<size_t>(row) * H + k0 + c * 8 : zero16;
+        const int row = min(m0 + r, T - 1);
+        const uint16_t* src = a_planes + p * a_plane + static_cast<size_t>(row) * H + k0 + c * 8;
         __builtin_amdgcn_global_load_lds(src, base + i * 1024, 16, 0, 0);
     }
 }
 
+// Eight FP32 weights (two float4) -> their three BF16 planes as MFMA B
+// fragments: W = W0 + W1 + W2 exactly, each plane the round-to-nearest-even
+// BF16 of what the previous planes left.
+__device__ __forceinline__ void split_fragment(const float4 (&w)[2], bf16x8_t& b0, bf16x8_t& b1, bf16x8_t& b2) {
+    const float v[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+    u32x4 q0, q1, q2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float x0 = v[2 * j], x1 = v[2 * j + 1];
+        const uint32_t p0 = cvt_pk_bf16(x0, x1);
+        const float r0 = x0 - bf16_lo(p0), r1 = x1 - bf16_hi(p0);
+        const uint32_t p1 = cvt_pk_bf16(r0, r1);
+        const uint32_t p2 = cvt_pk_bf16(r0 - bf16_lo(p1), r1 - bf16_hi(p1));
+        q0[j] = p0;
+        q1[j] = p1;
+        q2[j] = p2;
+    }
+    b0 = __builtin_bit_cast(bf16x8_t, q0);
+    b1 = __builtin_bit_cast(bf16x8_t, q1);
+    b2 = __builtin_bit_cast(bf16x8_t, q2);
+}
+
 // Block b works on K-slice b % nsplit and tile b / nsplit. Blocks go to the
 // eight XCDs round-robin, so when nsplit divides 8 every XCD only ever reads
-// one K-slice of the weight planes and keeps it in its own L2.
-template <int NA, int MT, int NT>
+// one K-slice of the weights and keeps it in its own L2.
+//
+// PRESPLIT: the weights come as split_weight_kernel's fragment-ordered
+// planes (w_frags), one 16-byte load per lane and fragment. Otherwise they
+// come as the FP32 rows of W and each wave splits its own: for many tokens
+// the split, repeated by every row tile, costs the MFMA loop more (about 7%
+// at 4096-8192 tokens) than one split kernel per call, for few tokens less.
+template <int NA, int MT, int NT, bool PRESPLIT>
 __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2))) void proj_kernel(
-    const uint16_t* __restrict__ a_planes, const uint16_t* __restrict__ w_frags,
-    const uint16_t* __restrict__ zero16, int T, int H, int E, int kslice, int nsplit,
-    int tiles_m, float* __restrict__ partials) {
+    const uint16_t* __restrict__ a_planes, const float* __restrict__ W, const uint16_t* __restrict__ w_frags,
+    int T, int H, int E, int kslice, int nsplit, int tiles_m, float* __restrict__ partials) {
     using S = GemmShape<NA, MT, NT>;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x;
@@ -192,9 +223,6 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
     const int kend = min(H, kbeg + kslice);
     const int nst = (kend - kbeg) / kKC;
     const size_t a_plane = static_cast<size_t>(T) * H;
-    // this tile's fragments, from the first K-step of the slice
-    const bf16x8_t* frags = reinterpret_cast<const bf16x8_t*>(w_frags) +
-                            (static_cast<size_t>(n_tile) * (H / kKC) + kbeg / kKC) * (3 * S::G * kWave);
 
     f32x16_t acc[MT][NT];
 #pragma unroll
@@ -204,20 +232,43 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
-    bf16x8_t bq[2][3][NT];
-    auto load_b = [&](int s, bf16x8_t (&b)[3][NT]) {
-        const bf16x8_t* src = frags + static_cast<size_t>(s) * (3 * S::G * kWave);
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) b[p][nt] = src[(p * S::G + wave * NT + nt) * kWave + lane];
-    };
-
     const int frow = lane & 31;
     const int c = lane >> 5;   // chunk: K columns [8c, 8c + 8) of the step
-    if (nst > 0) load_b(0, bq[0]);
+    // B operand of accumulator column group nt: expert n0 + 32 (wave NT + nt)
+    // + (lane & 31), K columns [16 s + 8 c, +8) of step s; experts past E
+    // read expert E - 1 (their results are never stored)
+    const float* wrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int e = min(n0 + (wave * NT + nt) * 32 + frow, E - 1);
+        wrow[nt] = W + static_cast<size_t>(e) * H + kbeg + 8 * c;
+    }
+    float4 wq[2][NT][2];      // FP32 weights of two steps
+    bf16x8_t bq[2][3][NT];    // (PRESPLIT) fragments of two steps
+    // this tile's fragments, from the first K-step of the slice
+    constexpr int G = S::BN / 32;   // fragments per plane and K-step
+    const bf16x8_t* frags = reinterpret_cast<const bf16x8_t*>(w_frags) +
+                            (static_cast<size_t>(n_tile) * (H / kKC) + kbeg / kKC) * (3 * G * kWave);
+    auto load_b = [&](int s, int set) {
+        if constexpr (PRESPLIT) {
+            const bf16x8_t* src = frags + static_cast<size_t>(s) * (3 * G * kWave);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) bq[set][p][nt] = src[(p * G + wave * NT + nt) * kWave + lane];
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float4* src = reinterpret_cast<const float4*>(wrow[nt] + s * kKC);
+                wq[set][nt][0] = src[0];
+                wq[set][nt][1] = src[1];
+            }
+        }
+    };
+
+    if (nst > 0) load_b(0, 0);
     for (int s = 0; s < kARing - 1 && s < nst; ++s)
-        issue_a<S>(lds + s * S::STAGE, kbeg + s * kKC, wave, lane, m0, T, H, a_planes, a_plane, zero16);
+        issue_a<S>(lds + s * S::STAGE, kbeg + s * kKC, wave, lane, m0, T, H, a_planes, a_plane);
     for (int s0 = 0; s0 < nst; s0 += 2) {
 #pragma unroll
         for (int ph = 0; ph < 2; ++ph) {
@@ -227,10 +278,20 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
                 // every wave's: stage s is complete and stage s-1 is free
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
-                if (s + 1 < nst) load_b(s + 1, bq[ph ^ 1]);
+                bf16x8_t b[3][NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    if constexpr (PRESPLIT) {
+#pragma unroll
+                        for (int p = 0; p < 3; ++p) b[p][nt] = bq[ph][p][nt];
+                    } else {
+                        split_fragment(wq[ph][nt], b[0][nt], b[1][nt], b[2][nt]);
+                    }
+                }
+                if (s + 1 < nst) load_b(s + 1, ph ^ 1);
                 if (s + kARing - 1 < nst)
                     issue_a<S>(lds + ((s + kARing - 1) % kARing) * S::STAGE, kbeg + (s + kARing - 1) * kKC,
-                               wave, lane, m0, T, H, a_planes, a_plane, zero16);
+                               wave, lane, m0, T, H, a_planes, a_plane);
                 const char* base = lds + (s % kARing) * S::STAGE;
                 bf16x8_t a[NA][MT];
 #pragma unroll
@@ -249,7 +310,7 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
                     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt)
-                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[q]][mt], bq[ph][PB[q]][nt],
+                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[q]][mt], b[PB[q]][nt],
                                                                                   acc[mt][nt], 0, 0, 0);
             }
         }
@@ -272,11 +333,17 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
         }
 }
 
-// Workspace layout: [zero block 256 B][W planes][input planes (FP32 input)][partials].
+// From this many tokens the weights are split once per call into
+// fragment-ordered planes; below, each wave splits the FP32 weights it loads.
+constexpr int kPresplitTokens = 4096;
+
+// Workspace layout: [W planes (from kPresplitTokens)][input planes (FP32
+// input)][partials].
 struct RoutePlan {
     int na, mt, nt;                 // kernel variant
+    bool presplit;
     int tiles_m, tiles_n, nsplit, kslice;
-    size_t zero_bytes, w_planes_bytes, a_planes_bytes, partial_bytes;
+    size_t w_planes_bytes, a_planes_bytes, partial_bytes;
 };
 
 inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
@@ -298,26 +365,31 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
     const int per = ceil_div(chunks, ns);   // K stages per split
     p.kslice = per * kKC;
     p.nsplit = ceil_div(H, p.kslice);
-    p.zero_bytes = 256;
+    p.presplit = T >= kPresplitTokens;
     // fragment-ordered planes, padded to whole expert tiles
-    p.w_planes_bytes = round256(static_cast<size_t>(3) * p.tiles_n * 128 * p.nt * H * sizeof(uint16_t));
+    p.w_planes_bytes = p.presplit ? round256(static_cast<size_t>(3) * p.tiles_n * 128 * p.nt * H * sizeof(uint16_t)) : 0;
     p.a_planes_bytes = p.na == 3 ? round256(static_cast<size_t>(3) * T * H * sizeof(uint16_t)) : 0;
     p.partial_bytes = round256(static_cast<size_t>(p.nsplit) * T * E * sizeof(float));
     return p;
 }
 
 template <int NA, int MT, int NT>
-int launch_proj(const RoutePlan& p, const uint16_t* a, const uint16_t* w, const uint16_t* zero,
-                int T, int H, int E, float* partials, void* stream) {
+int launch_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uint16_t* w_frags, int T, int H,
+                int E, float* partials, void* stream) {
     using S = GemmShape<NA, MT, NT>;
-    return launch(proj_kernel<NA, MT, NT>, dim3(p.tiles_m * p.tiles_n * p.nsplit), dim3(kGemmBlock),
-                  S::LDS, stream, a, w, zero, T, H, E, p.kslice, p.nsplit, p.tiles_m, partials);
+    const dim3 grid(p.tiles_m * p.tiles_n * p.nsplit);
+    if (p.presplit)
+        return launch(proj_kernel<NA, MT, NT, true>, grid, dim3(kGemmBlock), S::LDS, stream, a, W, w_frags, T, H,
+                      E, p.kslice, p.nsplit, p.tiles_m, partials);
+    return launch(proj_kernel<NA, MT, NT, false>, grid, dim3(kGemmBlock), S::LDS, stream, a, W, w_frags, T, H, E,
+                  p.kslice, p.nsplit, p.tiles_m, partials);
 }
 
-int run_proj(const RoutePlan& p, const uint16_t* a, const uint16_t* w, const uint16_t* zero, int T,
-             int H, int E, float* partials, void* stream) {
+int run_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uint16_t* w_frags, int T, int H,
+             int E, float* partials, void* stream) {
 #define MOE_PROJ(NA, MT, NT) \
-    if (p.na == NA && p.mt == MT && p.nt == NT) return launch_proj<NA, MT, NT>(p, a, w, zero, T, H, E, partials, stream);
+    if (p.na == NA && p.mt == MT && p.nt == NT) \
+        return launch_proj<NA, MT, NT>(p, a, W, w_frags, T, H, E, partials, stream);
     MOE_PROJ(1, 1, 1) MOE_PROJ(1, 1, 2) MOE_PROJ(1, 2, 1) MOE_PROJ(1, 2, 2) MOE_PROJ(1, 4, 1) MOE_PROJ(1, 4, 2)
     MOE_PROJ(3, 1, 1) MOE_PROJ(3, 1, 2) MOE_PROJ(3, 2, 1) MOE_PROJ(3, 2, 2)
 #undef MOE_PROJ
@@ -332,7 +404,7 @@ extern "C" size_t moe_route_workspace_bytes(int T, int H, int E, int k, int hidd
     if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || logits_in) return 0;
     if (hidden_dtype != MOE_DTYPE_F32 && hidden_dtype != MOE_DTYPE_BF16) return 0;
     const RoutePlan p = plan_route(T, H, E, hidden_dtype);
-    return p.zero_bytes + p.w_planes_bytes + p.a_planes_bytes + p.partial_bytes;
+    return p.w_planes_bytes + p.a_planes_bytes + p.partial_bytes;
 }
 
 extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, const float* bias,
@@ -361,28 +433,29 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
     if (!aligned16(workspace)) return MOE_ERR_ALIGN;
     const RoutePlan p = plan_route(T, H, E, hidden_dtype);
     char* ws = static_cast<char*>(workspace);
-    uint16_t* zero = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* w_planes = reinterpret_cast<uint16_t*>(ws + p.zero_bytes);
-    uint16_t* a_planes = reinterpret_cast<uint16_t*>(ws + p.zero_bytes + p.w_planes_bytes);
-    float* partials = reinterpret_cast<float*>(ws + p.zero_bytes + p.w_planes_bytes + p.a_planes_bytes);
+    uint16_t* w_planes = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* a_planes = reinterpret_cast<uint16_t*>(ws + p.w_planes_bytes);
+    float* partials = reinterpret_cast<float*>(ws + p.w_planes_bytes + p.a_planes_bytes);
 
     const int cap = device_cu_count() * 8;
-    const int G = 4 * p.nt;   // 32-expert groups per expert tile
-    const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * G * kWave;   // threads
-    const int gw = ceil_div(wslots, 256);
-    int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, G,
-                    p.tiles_n, reinterpret_cast<u32x4*>(w_planes), reinterpret_cast<uint32_t*>(zero));
-    if (rc) return rc;
+    if (p.presplit) {
+        const int G = 4 * p.nt;   // 32-expert groups per expert tile
+        const long long wslots = static_cast<long long>(p.tiles_n) * (H / kKC) * G * kWave;   // threads
+        const int gw = ceil_div(wslots, 256);
+        const int rc = launch(split_weight_kernel, dim3(gw < cap ? gw : cap), dim3(256), 0, stream, W, E, H, G,
+                              p.tiles_n, reinterpret_cast<u32x4*>(w_planes));
+        if (rc) return rc;
+    }
     const uint16_t* a = static_cast<const uint16_t*>(hidden);
     if (p.na == 3) {
         const size_t an = static_cast<size_t>(T) * H;
         const int ga = ceil_div(static_cast<long long>(an), 256 * 4);
-        rc = launch(split3_kernel, dim3(ga < cap ? ga : cap), dim3(256), 0, stream,
-                    static_cast<const float*>(hidden), an, a_planes);
+        const int rc = launch(split3_kernel, dim3(ga < cap ? ga : cap), dim3(256), 0, stream,
+                              static_cast<const float*>(hidden), an, a_planes);
         if (rc) return rc;
         a = a_planes;
     }
-    rc = run_proj(p, a, w_planes, zero, T, H, E, partials, stream);
+    const int rc = run_proj(p, a, W, w_planes, T, H, E, partials, stream);
     if (rc) return rc;
     return run_select(partials, p.nsplit, scale, 0, bias, token_mask, T, E, k, logits, topk_ids,
                       topk_w, stream);

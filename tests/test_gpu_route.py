@@ -99,7 +99,11 @@ def test_route_full_size_sampled(name):
 
 def test_route_scale_and_ragged_shapes():
     g = np.random.default_rng(60)
-    for T, H, E, k in [(1, 16, 1, 1), (3, 48, 5, 5), (70, 1040, 200, 6), (129, 256, 64, 32), (33, 4096, 4096, 8), (9, 16384, 64, 4)]:
+    # below 4096 tokens the projection splits the weights in registers, from
+    # 4096 it reads planes split by a kernel of their own: both with a ragged
+    # token tile and a padded expert tile
+    for T, H, E, k in [(1, 16, 1, 1), (3, 48, 5, 5), (70, 1040, 200, 6), (129, 256, 64, 32), (33, 4096, 4096, 8),
+                       (9, 16384, 64, 4), (4100, 272, 300, 8)]:
         note("route ragged T=%d H=%d E=%d k=%d" % (T, H, E, k))
         hidden = wl.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
         W = (g.standard_normal((E, H)) * 0.02).astype(np.float32)
