@@ -21,7 +21,9 @@
 // When the tile histograms are small (tiles^2 * E below kFuseLimit, every
 // shape up to tens of thousands of slots), step 2 is folded into step 3:
 // each place block sums the histograms itself -- its own exclusive prefix
-// over the tiles and every expert's total -- which saves a launch.
+// over the tiles and every expert's total -- which saves a launch. With one
+// tile (up to 1024 slots) step 1 goes too: the place block's per-wave
+// histograms are the only ones, and their sums are the totals.
 #include <cmath>
 
 #include "launch.hpp"
@@ -146,12 +148,16 @@ __device__ __forceinline__ void place_chunk(int id, int f, int n, int E, int idb
     }
 }
 
-// LDS layout: off[E + 1], hist[kDispWaves][E], then (FUSED) cnt[E], rel[E].
-// FUSED: tile_hist holds the raw tile histograms; the block derives the
-// expert totals (block 0 writes them to counts) and its exclusive prefix
-// over the tiles. Otherwise tile_hist holds the prefixes and counts the
-// totals, from scan_kernel.
-template <bool FUSED>
+// How the place step learns the expert totals and its tile's prefix.
+enum PlaceMode {
+    kPlaceScanned = 0,   // tile_hist holds the prefixes and counts the totals, from scan_kernel
+    kPlaceFused = 1,     // tile_hist holds the raw tile histograms; the block sums them itself
+    kPlaceSingle = 2     // one tile: its per-wave histograms give the totals (no hist_kernel)
+};
+
+// LDS layout: off[E + 1], hist[kDispWaves][E], then (fused, single) cnt[E],
+// rel[E]. Block 0 writes the totals to counts in the fused and single modes.
+template <int MODE>
 __global__ __launch_bounds__(kDispBlock) void place_kernel(
     const int32_t* __restrict__ ids, int n, int E, int tile, int tiles,
     const int32_t* __restrict__ tile_hist, int32_t* __restrict__ counts,
@@ -179,7 +185,37 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     }
     const int32_t* cnt = counts;
     const int32_t* rel = tile_hist + static_cast<size_t>(blockIdx.x) * E;
-    if (FUSED) {
+    int32_t* my = hist + wave * E;
+    if (MODE == kPlaceSingle) {
+        // step (2) first: the per-wave histograms, then the totals from them
+        for (int e = tid; e < kDispWaves * E; e += kDispBlock) hist[e] = 0;
+        __syncthreads();
+        if (cached) {
+#pragma unroll
+            for (int c = 0; c < kIdChunks; ++c)
+                if (idr[c] >= 0) atomicAdd(&my[idr[c]], 1);
+        } else {
+            for (int i = lane; i < quarter; i += kWave) {
+                const int id = slot_id(ids, q0 + i, n, E);
+                if (id >= 0) atomicAdd(&my[id], 1);
+            }
+        }
+        __syncthreads();
+        int32_t* cnt_l = hist + kDispWaves * E;
+        int32_t* rel_l = cnt_l + E;
+        for (int e = tid; e < E; e += kDispBlock) {
+            int total = 0;
+#pragma unroll
+            for (int w = 0; w < kDispWaves; ++w) total += hist[w * E + e];
+            cnt_l[e] = total;
+            rel_l[e] = 0;
+            counts[e] = total;
+        }
+        __syncthreads();
+        cnt = cnt_l;
+        rel = rel_l;
+    }
+    if (MODE == kPlaceFused) {
         int32_t* cnt_l = hist + kDispWaves * E;
         int32_t* rel_l = cnt_l + E;
         for (int e = tid; e < E; e += kDispBlock) {
@@ -217,7 +253,8 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
         if (lane >= d) incl += o;
     }
     if (lane == kWave - 1) wsum[wave] = incl;
-    for (int e = tid; e < kDispWaves * E; e += kDispBlock) hist[e] = 0;
+    if (MODE != kPlaceSingle)
+        for (int e = tid; e < kDispWaves * E; e += kDispBlock) hist[e] = 0;
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wsum[w];
@@ -232,19 +269,20 @@ __global__ __launch_bounds__(kDispBlock) void place_kernel(
     if (blockIdx.x == 0)
         for (int e = tid; e <= E; e += kDispBlock) offsets[e] = off[e];
 
-    // (2) per-wave histograms of the tile's quarters.
-    int32_t* my = hist + wave * E;
-    if (cached) {
+    // (2) per-wave histograms of the tile's quarters (done above for one tile).
+    if (MODE != kPlaceSingle) {
+        if (cached) {
 #pragma unroll
-        for (int c = 0; c < kIdChunks; ++c)
-            if (idr[c] >= 0) atomicAdd(&my[idr[c]], 1);
-    } else {
-        for (int i = lane; i < quarter; i += kWave) {
-            const int id = slot_id(ids, q0 + i, n, E);
-            if (id >= 0) atomicAdd(&my[id], 1);
+            for (int c = 0; c < kIdChunks; ++c)
+                if (idr[c] >= 0) atomicAdd(&my[idr[c]], 1);
+        } else {
+            for (int i = lane; i < quarter; i += kWave) {
+                const int id = slot_id(ids, q0 + i, n, E);
+                if (id >= 0) atomicAdd(&my[id], 1);
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
     // (3) starting position of each wave's run of each expert.
     for (int e = tid; e < E; e += kDispBlock) {
         int p = off[e] + rel[e];
@@ -311,17 +349,21 @@ extern "C" int moe_dispatch(const int32_t* topk_ids, int T, int k, int E, int32_
     if (!aligned16(workspace)) return MOE_ERR_ALIGN;
     const TilePlan p = plan_tiles(n);
     int32_t* tile_counts = static_cast<int32_t*>(workspace);
+    const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) + 1 + static_cast<size_t>(kDispWaves) * E);
+    if (p.tiles == 1)   // one tile: the place step counts it itself
+        return launch(place_kernel<kPlaceSingle>, dim3(1), dim3(kDispBlock), lds + sizeof(int32_t) * 2 * E,
+                      stream, topk_ids, p.n, E, p.tile, p.tiles, static_cast<const int32_t*>(tile_counts),
+                      counts, offsets, perm, dest);
     int rc = launch(hist_kernel, dim3(p.tiles), dim3(kDispBlock), sizeof(int32_t) * E, stream,
                     topk_ids, p.n, E, p.tile, tile_counts);
     if (rc) return rc;
-    const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) + 1 + static_cast<size_t>(kDispWaves) * E);
     if (static_cast<long long>(p.tiles) * p.tiles * E <= kFuseLimit)
-        return launch(place_kernel<true>, dim3(p.tiles), dim3(kDispBlock), lds + sizeof(int32_t) * 2 * E,
+        return launch(place_kernel<kPlaceFused>, dim3(p.tiles), dim3(kDispBlock), lds + sizeof(int32_t) * 2 * E,
                       stream, topk_ids, p.n, E, p.tile, p.tiles, static_cast<const int32_t*>(tile_counts),
                       counts, offsets, perm, dest);
     rc = launch(scan_kernel, dim3(ceil_div(E, kWave)), dim3(kDispBlock), 0, stream, tile_counts,
                 p.tiles, E, counts);
     if (rc) return rc;
-    return launch(place_kernel<false>, dim3(p.tiles), dim3(kDispBlock), lds, stream, topk_ids, p.n, E,
+    return launch(place_kernel<kPlaceScanned>, dim3(p.tiles), dim3(kDispBlock), lds, stream, topk_ids, p.n, E,
                   p.tile, p.tiles, static_cast<const int32_t*>(tile_counts), counts, offsets, perm, dest);
 }

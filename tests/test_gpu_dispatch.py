@@ -38,7 +38,9 @@ def test_dispatch_workloads(name):
         assert counts[hot].sum() == w.T * w.k        # every pick on the 16 hot experts
 
 
-@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (3, 2, 5, 1), (100, 7, 33, 2), (1000, 8, 256, 3),
+# up to 1024 slots are one tile, which the place kernel counts itself
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (3, 2, 5, 1), (100, 7, 33, 2), (200, 5, 4096, 7),
+                                         (32, 32, 3, 8), (205, 5, 17, 9), (1000, 8, 256, 3),
                                          (4099, 5, 4096, 4), (2047, 32, 64, 5), (70001, 3, 1000, 6)])
 def test_dispatch_random_ids(T, k, E, seed):
     g = np.random.default_rng(seed)
@@ -52,6 +54,7 @@ def test_dispatch_all_one_expert_and_all_invalid():
     _check(np.full((T, k), E - 1, np.int32), E, "one expert")
     _check(np.full((T, k), -1, np.int32), E, "all invalid")
     _check(np.zeros((T, 1), np.int32), 1, "E=1")
+    _check(np.full((100, 8), -1, np.int32), 64, "all invalid, one tile")
 
 
 def test_dispatch_zero_tokens():
