@@ -161,6 +161,28 @@ def test_route_exact_ties_all_equal():
         np.testing.assert_array_equal(host(wt), w_o)
 
 
+@pytest.mark.parametrize("E,k", [(512, 22), (512, 11), (300, 12), (128, 16), (64, 32), (40, 13)])
+def test_route_logits_in_ties_many_picks(E, k):
+    """From 12 picks the selection searches the k-th largest key bit by bit
+    (below, it takes k rounds): logits on a coarse grid (many exact key
+    ties, across the k-th place too), a few NaN logits (keys below every
+    number) and a coarse bias, against the oracle bit for bit."""
+    require_gpu()
+    g = np.random.default_rng(E + k)
+    T = 64
+    lg = (g.integers(-6, 7, size=(T, E)) / 4).astype(np.float32)
+    lg[g.uniform(size=(T, E)) < 0.02] = np.nan
+    lg[3] = 0.0                                               # one token all equal
+    bias = (g.integers(-2, 3, E) / 32).astype(np.float32)
+    mask = np.ones(T, np.uint8)
+    mask[7] = 0
+    note("route logits-in ties E=%d k=%d" % (E, k))
+    _, ids, wt = m.route(None, None, dev(bias), dev(mask), k, logits=dev(lg))
+    ids_o, w_o = O.route_from_logits(lg, bias, mask, k)
+    np.testing.assert_array_equal(host(ids), ids_o)
+    np.testing.assert_array_equal(host(wt), w_o)
+
+
 def test_route_mask_with_nan_rows():
     w = wl.WORKLOADS["prefill"]
     T = 256
