@@ -295,12 +295,14 @@ def main():
     if args.schedule == "auto":
         args.schedule = "overlap" if T >= 2048 else "serial"
     head_step = {"overlap": step_overlap, "overlap-route": step_overlap_route, "serial": step_serial}[args.schedule]
-    # warm up eagerly on a side stream (as graph capture requires), then capture
+    # one step on a side stream (graph capture wants the work seen once off
+    # the capture stream), then the W warm-up steps on the launch stream
+    # itself, eager or replayed, so that nothing first-time lands in the
+    # timed steps
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        for _ in range(max(1, args.warmup)):
-            head_step()
+        head_step()
     stream.wait_stream(side)
     torch.cuda.synchronize()
     if args.graph:
@@ -309,10 +311,11 @@ def main():
             head_step()
         torch.cuda.synchronize()
         head_fn = graph.replay
-        for _ in range(args.warmup):
-            head_fn()
     else:
         head_fn = head_step
+    for _ in range(args.warmup):
+        head_fn()
+    torch.cuda.synchronize()
 
     # headline: exactly K steps between two synchronizations
     ms_per_step = timed(head_fn, args.steps)
