@@ -28,7 +28,8 @@ Alongside the throughput the line carries:
   stages        per-call mean duration (HIP events on the launch stream, from
                 a serial eager pass) and algorithmic bytes / achieved GB/s
   schedules     ms per step of every schedule, and of the serial one with the
-                256 MB last-level cache flushed before each step (cold)
+                256 MB last-level cache flushed before each step (cold); the
+                p10 / median / p90 of single serial steps (HIP events)
   roofline      the dominant kernel (the combine) against MI355X's 8 TB/s:
                 algorithmic bytes per launch / mean launch duration; `traffic`
                 is the HBM bytes per launch from the committed rocprofv3
@@ -398,6 +399,11 @@ def main():
     total_bytes = sum(nbytes.values())
     stages = {n: {"ms": round(stage_ms[n], 4), "bytes": nbytes[n],
                   "GBps": round(nbytes[n] / (stage_ms[n] * 1e-3) / 1e9, 1)} for n in names}
+    # per-step spread of the serial pass (first call's start to last call's end)
+    step_ev = np.array([events[i][0].elapsed_time(events[i][4]) for i in range(args.steps)])
+    serial_spread = {"p10_ms": round(float(np.percentile(step_ev, 10)), 4),
+                     "median_ms": round(float(np.median(step_ev)), 4),
+                     "p90_ms": round(float(np.percentile(step_ev, 90)), 4)}
     proj_flop = 2.0 * T * H * E
     if rank_block is not None:
         rank_block["GBps"] = round(nbytes["norm_quant"] / (rank_block["ms"] * 1e-3) / 1e9, 1)
@@ -453,7 +459,8 @@ def main():
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),
                       "overlap_graph_ms": round(overlap_graph_ms, 4),
                       "serial_graph_ms": round(serial_graph_ms, 4),
-                      "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4)},
+                      "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4),
+                      "serial_steps": serial_spread},
         "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),
         "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(comb_gbs, 1),
