@@ -192,6 +192,31 @@ def test_fc1_swiglu_small(T, k, E, K, N, invalid, skew):
     print("boundary blocks %d of %d, code mismatches inside %d" % (nset, near.size, nmis))
 
 
+def test_fc1_swiglu_tails():
+    """Gate values far into silu's tails: the weights' global scales are
+    small, so gate and up values reach the hundreds and beyond and silu(g)
+    ranges from g itself (g > 0) through subnormal negative values (g in
+    about -104..-87, whose FP32 evaluation may flush to zero: the boundary
+    set flags those blocks) to an exact zero."""
+    T, k, E, K, N = 48, 2, 3, 64, 64
+    g = np.random.default_rng(5)
+    w = wl.WORKLOADS["wide_k"]
+    xp, xs = wl.fc1_activations(w, T, K)
+    wp, ws, gw = wl.fc1_weights(w, 2 * N, E, K)
+    gw = np.array([2.0 ** -6, 2.5, 0.5], np.float32)   # gates up to ~2e4, ~150 and ~800
+    perm, offsets = _routing(g, T, k, E)
+    gx = np.float32(4.0)
+    args = (xp, xs, gx, perm, offsets, k, wp, ws, gw)
+    acc, _ = O.fc1_exact(*args)
+    assert acc[:, :N].min() < -100 and acc[:, :N].max() > 100
+    gy = O.global_scale(_swiglu_values(acc))
+    got_p, got_s = _run_swiglu(*args, gy, "tails")
+    ref_p, ref_s = O.expert_fc1_swiglu_nvfp4(*args, gy)
+    near = O.fc1_swiglu_boundary_blocks(*args, gy)
+    nset, nmis = _check(got_p, got_s, ref_p, ref_s, near, "fc1 swiglu tails")
+    print("boundary blocks %d of %d, code mismatches inside %d" % (nset, near.size, nmis))
+
+
 def test_fc1_swiglu_and_relu2_share_the_grouping():
     """Same input, grouping and weight bytes: the SwiGLU call over 2N rows and
     the Relu2 call over the same 2N rows both leave the rows past the routed

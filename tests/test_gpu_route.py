@@ -102,8 +102,10 @@ def test_route_scale_and_ragged_shapes():
     # below 4096 tokens the projection splits the weights in registers, from
     # 4096 it reads planes split by a kernel of their own: both with a ragged
     # token tile and a padded expert tile
+    # (token tiles of 32, 64 or 128 rows by count: 3000 takes 128-row tiles
+    # with the in-register split)
     for T, H, E, k in [(1, 16, 1, 1), (3, 48, 5, 5), (70, 1040, 200, 6), (129, 256, 64, 32), (33, 4096, 4096, 8),
-                       (9, 16384, 64, 4), (4100, 272, 300, 8)]:
+                       (9, 16384, 64, 4), (3000, 512, 256, 8), (4100, 272, 300, 8)]:
         note("route ragged T=%d H=%d E=%d k=%d" % (T, H, E, k))
         hidden = wl.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
         W = (g.standard_normal((E, H)) * 0.02).astype(np.float32)
@@ -113,14 +115,17 @@ def test_route_scale_and_ragged_shapes():
         _check_projection(hidden, W, bias, mask, k, 0.75, np.arange(T), "ragged %d/%d/%d/%d" % (T, H, E, k))
 
 
-def test_route_fp32_input():
+@pytest.mark.parametrize("T", [300, 4100])
+def test_route_fp32_input(T):
+    """FP32 hidden states (three input planes): 300 tokens split the weights
+    in registers, 4100 read the split kernel's planes."""
     w = wl.WORKLOADS["tiny"]
     g = np.random.default_rng(61)
-    hidden = (g.standard_normal((300, w.H)) * 3).astype(np.float32)
+    hidden = (g.standard_normal((T, w.H)) * 3).astype(np.float32)
     W = wl.router_weight(w)
     bias = wl.bias(w)
-    mask = np.ones(300, np.uint8)
-    _check_projection(hidden, W, bias, mask, w.k, 1.0, np.arange(300), "fp32 input")
+    mask = np.ones(T, np.uint8)
+    _check_projection(hidden, W, bias, mask, w.k, 1.0, np.arange(T), "fp32 input %d" % T)
 
 
 def test_route_logits_in_tie_run():
