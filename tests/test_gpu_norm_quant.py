@@ -98,6 +98,31 @@ def test_norm_quant_widths(H):
     assert (s[3] == 0).all() and (p[3] == 0).all()
 
 
+@pytest.mark.parametrize("T,H", [(9001, 1024), (4000, 4096), (3000, 8192), (1500, 12288), (1000, 16384)])
+def test_norm_quant_blocks_visit_several_tokens(T, H):
+    """Token counts past what fits on the GPU at once (256 CUs at up to 8
+    waves per SIMD: 2048 blocks of 4 waves) for every width whose tokens fill
+    whole waves (H = 1024: four tokens per block) or the whole block (H a
+    multiple of 4096): blocks then loop over several tokens and copy each
+    next row into LDS ahead. Ragged counts leave blocks with one token fewer
+    and, at H = 1024, a last block with idle waves. Every row checked."""
+    g = np.random.default_rng(T + H)
+    x = wl.f32_to_bf16_bits((g.standard_normal((T, H)) * 3).astype(np.float32))
+    x[T - 1] = 0                                       # an all-zero last row
+    x[T // 2, 16:32] = 0x8000                          # negative zeros
+    nw = g.uniform(-1, 1, H).astype(np.float32)
+    gs = O.global_scale(O.rmsnorm_bf16(x, nw, 1.0, 1e-6))
+    p, s = _run(x, nw, 1.0, 1e-6, gs, "several tokens per block")
+    _check(x, nw, 1.0, 1e-6, gs, p, s, np.arange(T), "T=%d H=%d" % (T, H))
+    assert (s[T - 1] == 0).all() and (p[T - 1] == 0).all()
+    if H == 8192:
+        pooled = _gather_shards(x, 4)
+        note("norm_quant rank block T=%d H=%d tp=4" % (T, H))
+        pr, sr = m.norm_quant_nvfp4_rank_block(dev(pooled), T, dev(nw), 1.0, 1e-6, scalar_dev(gs))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pr), p) and np.array_equal(host(sr), s)
+
+
 def test_norm_quant_zero_tokens():
     require_gpu()
     p, s = m.norm_quant_nvfp4(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda:0"),
