@@ -55,29 +55,7 @@ __device__ __forceinline__ float sigmoid_rn(float l) {
 }
 
 constexpr int kSplitBatch = 8;   // split partials loaded before they are added
-
-// logit of (t, e): the split partial sums in order, times the scale (and
-// stored), or the caller's logit. The partials of a batch are all loaded
-// before the first of them is added, so their latencies overlap; the sum
-// still runs over the splits in order.
-__device__ __forceinline__ float token_logit(const float* __restrict__ partials, int nsplit,
-                                             size_t plane, float scale, int logits_in,
-                                             float* __restrict__ logits, size_t idx) {
-    if (logits_in) return logits[idx];
-    float s = partials[idx];
-#pragma unroll 1
-    for (int p0 = 1; p0 < nsplit; p0 += kSplitBatch) {
-        float q[kSplitBatch];
-#pragma unroll
-        for (int u = 0; u < kSplitBatch; ++u) q[u] = p0 + u < nsplit ? partials[(p0 + u) * plane + idx] : 0.f;
-#pragma unroll
-        for (int u = 0; u < kSplitBatch; ++u)
-            if (p0 + u < nsplit) s += q[u];
-    }
-    const float l = s * scale;
-    logits[idx] = l;
-    return l;
-}
+constexpr int kLdsBatch = 8;     // a lane's experts loaded (or scanned) at once by select_lds_kernel
 
 // One round's winner given this lane's best remaining candidate (has, bk, be):
 // the largest key, and among equal keys the lowest expert id.
@@ -327,12 +305,45 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     float* lgs = reinterpret_cast<float*>(keys + E);
     const size_t plane = static_cast<size_t>(T) * E;
     const bool valid = token_mask[t] != 0;
+    // the lane's experts e = lane + 64 i, kLdsBatch at a time: their logits
+    // (or split partials, split by split) are all loaded before any is used,
+    // so the loads overlap; each logit still sums its splits in order
 #pragma unroll 1
-    for (int e = lane; e < E; e += kWave) {
-        const float l = token_logit(partials, nsplit, plane, scale, logits_in, logits,
-                                    static_cast<size_t>(t) * E + e);
-        lgs[e] = l;
-        keys[e] = valid ? ordered_key(sigmoid_rn(l) + bias[e]) : 0u;
+    for (int e0 = lane; e0 < E; e0 += kLdsBatch * kWave) {
+        float l[kLdsBatch];
+#pragma unroll
+        for (int u = 0; u < kLdsBatch; ++u) {
+            const int e = e0 + u * kWave;
+            const size_t idx = static_cast<size_t>(t) * E + e;
+            l[u] = e < E ? (logits_in ? logits[idx] : partials[idx]) : 0.f;
+        }
+        if (!logits_in) {
+#pragma unroll 1
+            for (int p = 1; p < nsplit; ++p) {
+                float q[kLdsBatch];
+#pragma unroll
+                for (int u = 0; u < kLdsBatch; ++u) {
+                    const int e = e0 + u * kWave;
+                    q[u] = e < E ? partials[p * plane + static_cast<size_t>(t) * E + e] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < kLdsBatch; ++u) l[u] += q[u];
+            }
+#pragma unroll
+            for (int u = 0; u < kLdsBatch; ++u) {
+                const int e = e0 + u * kWave;
+                l[u] *= scale;
+                if (e < E) logits[static_cast<size_t>(t) * E + e] = l[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kLdsBatch; ++u) {
+            const int e = e0 + u * kWave;
+            if (e < E) {
+                lgs[e] = l[u];
+                keys[e] = valid ? ordered_key(sigmoid_rn(l[u]) + bias[e]) : 0u;
+            }
+        }
     }
     int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
     float* w = topk_w + static_cast<size_t>(t) * k;
@@ -352,13 +363,20 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     for (int j = 0; j < k; ++j) {
         uint32_t bk = 0u;
         int bi = -1;
+        // the lane's keys in slot order, kLdsBatch LDS reads in flight at a
+        // time; a strictly larger key replaces the best, so among equal keys
+        // the lowest slot (lowest id) stays
 #pragma unroll 1
-        for (int i = 0; i < nloc; ++i) {
-            if (!((live >> i) & 1ull)) continue;
-            const uint32_t kv = keys[lane + kWave * i];
-            if (bi < 0 || kv > bk) {
-                bk = kv;
-                bi = i;
+        for (int i0 = 0; i0 < nloc; i0 += kLdsBatch) {
+            uint32_t kv[kLdsBatch];
+#pragma unroll
+            for (int u = 0; u < kLdsBatch; ++u) kv[u] = i0 + u < nloc ? keys[lane + kWave * (i0 + u)] : 0u;
+#pragma unroll
+            for (int u = 0; u < kLdsBatch; ++u) {
+                const int i = i0 + u;
+                const bool take = i < nloc && ((live >> i) & 1ull) && (bi < 0 || kv[u] > bk);
+                bk = take ? kv[u] : bk;
+                bi = take ? i : bi;
             }
         }
         const float bl = bi >= 0 ? lgs[lane + kWave * bi] : 0.f;
