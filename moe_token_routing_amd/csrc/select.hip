@@ -80,8 +80,23 @@ __device__ __forceinline__ void write_picks(int lane, int k, int my_id, float my
 
 // EPL consecutive floats at p (16-byte vector loads when `vec`, which the
 // caller sets when the row length keeps them aligned).
-template <int EPL>
+template <int EPL, bool FULL>
 __device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, int n, float (&v)[EPL]) {
+    if constexpr (FULL) {
+        // every lane owns EPL experts and rows are 16-byte aligned: plain
+        // vector loads, no bounds (the full-lane case is decided per launch)
+        if constexpr (EPL % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < EPL; i += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(p + i);
+                v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) v[i] = p[i];
+        }
+        return;
+    }
     if constexpr (EPL % 4 == 0) {
         if (vec) {
 #pragma unroll
@@ -101,7 +116,7 @@ __device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, 
 // are loaded before any of them is added: 8 keep the registers of many waves
 // per SIMD (large batches split K 8 ways); 32 cut the dependent rounds of
 // loads when a small batch split K many ways (64 at 128 tokens).
-template <int EPL, int BATCH, bool THRESHOLD>
+template <int EPL, int BATCH, bool THRESHOLD, bool FULL>
 __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
@@ -112,16 +127,17 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const size_t plane = static_cast<size_t>(T) * E;
     const bool valid = token_mask[t] != 0;
     const int e0 = EPL * lane;
-    const int n = E - e0 < EPL ? (E - e0 > 0 ? E - e0 : 0) : EPL;   // experts of this lane
-    const bool vec = (E % 4) == 0 && n == EPL;
+    // experts of this lane (FULL: E = EPL * 64, every lane owns EPL)
+    const int n = FULL ? EPL : (E - e0 < EPL ? (E - e0 > 0 ? E - e0 : 0) : EPL);
+    const bool vec = FULL || ((E % 4) == 0 && n == EPL);
     const size_t row = static_cast<size_t>(t) * E + e0;
 
     float lg[EPL];
     if (n > 0) {
         if (logits_in) {
-            load_run<EPL>(logits + row, vec, n, lg);
+            load_run<EPL, FULL>(logits + row, vec, n, lg);
         } else {
-            load_run<EPL>(partials + row, vec, n, lg);
+            load_run<EPL, FULL>(partials + row, vec, n, lg);
             // a batch of splits is loaded before any is added (the loads
             // overlap); the sum still runs over the splits in order
 #pragma unroll 1
@@ -130,7 +146,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u) {
                     if (p0 + u < nsplit) {
-                        load_run<EPL>(partials + (p0 + u) * plane + row, vec, n, q[u]);
+                        load_run<EPL, FULL>(partials + (p0 + u) * plane + row, vec, n, q[u]);
                     } else {
 #pragma unroll
                         for (int i = 0; i < EPL; ++i) q[u][i] = 0.f;
@@ -397,11 +413,17 @@ int launch_select_reg2(const float* partials, int nsplit, float scale, int logit
                        const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
                        void* stream) {
     const dim3 grid(ceil_div(T, kSelectWaves));
-    if (k >= kThresholdPicks)
-        return launch(select_reg_kernel<EPL, BATCH, true>, grid, dim3(kSelectBlock), 0, stream, partials, nsplit,
-                      scale, logits_in, bias, mask, T, E, k, logits, ids, w);
-    return launch(select_reg_kernel<EPL, BATCH, false>, grid, dim3(kSelectBlock), 0, stream, partials, nsplit,
-                  scale, logits_in, bias, mask, T, E, k, logits, ids, w);
+#define MOE_SELECT(THR, FULL)                                                                                 \
+    return launch(select_reg_kernel<EPL, BATCH, THR, FULL>, grid, dim3(kSelectBlock), 0, stream, partials, nsplit, \
+                  scale, logits_in, bias, mask, T, E, k, logits, ids, w)
+    const bool full = E == EPL * kWave;   // then E % 4 == 0 and every row is 16-byte aligned
+    if (k >= kThresholdPicks) {
+        if (full) MOE_SELECT(true, true);
+        MOE_SELECT(true, false);
+    }
+    if (full) MOE_SELECT(false, true);
+    MOE_SELECT(false, false);
+#undef MOE_SELECT
 }
 
 template <int EPL>
