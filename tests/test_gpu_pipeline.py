@@ -63,16 +63,21 @@ def test_pipeline_end_to_end(name, T):
     assert np.array_equal(r["scales"][rows][~near], rs[~near])
 
 
+@pytest.mark.parametrize("name", ["decode", "prefill"])
 @pytest.mark.parametrize("two_stream", [False, True])
-def test_pipeline_graph_replay(two_stream):
+def test_pipeline_graph_replay(name, two_stream):
     """Capture the four calls in a HIP graph -- on one stream, or with norm +
     quant forked onto a second stream beside route -> dispatch -> combine --
     and replay it with new inputs copied into the captured buffers; every
-    replay must equal a serial eager run bit for bit."""
+    replay must equal a serial eager run bit for bit. At 128 tokens and at
+    the 8192-token prefill batch, whose calls take their large-batch forms
+    (weight planes split by a kernel of their own, tile histograms summed in
+    the place step, norm + quant copying rows ahead, one block per token in
+    the combine)."""
     require_gpu()
-    w = wl.WORKLOADS["decode"]
+    w = wl.WORKLOADS[name]
     T = w.T
-    d = _inputs("decode")
+    d = _inputs(name)
     h_d, W_d, b_d, m_d = dev(d["hidden"]), dev(d["W"]), dev(d["bias"]), dev(d["mask"])
     x_d, qw_d, cg_d, eo_d = dev(d["x"]), dev(d["qw"]), dev(d["cg"]), dev(d["eo"])
     gs_d = scalar_dev(0.5)
@@ -122,12 +127,18 @@ def test_pipeline_graph_replay(two_stream):
     torch.cuda.synchronize()
     g = np.random.default_rng(12)
     for rep in range(3):
-        note("graph replay %d (two_stream=%s)" % (rep, two_stream))
+        note("graph replay %s %d (two_stream=%s)" % (name, rep, two_stream))
         # new inputs in place
-        h_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
-        x_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
-        mk = (g.uniform(size=T) > 0.2).astype(np.uint8)
-        m_d.copy_(dev(mk))
+        if name == "decode":
+            h_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
+            x_d.copy_(dev(wl.f32_to_bf16_bits(g.standard_normal((T, w.H)).astype(np.float32))))
+            mk = (g.uniform(size=T) > 0.2).astype(np.uint8)
+            m_d.copy_(dev(mk))
+        else:
+            gt = torch.Generator(device=DEV).manual_seed(12 + rep)
+            h_d.copy_(torch.randn((T, w.H), generator=gt, device=DEV).to(torch.bfloat16))
+            x_d.copy_(torch.randn((T, w.H), generator=gt, device=DEV).to(torch.bfloat16))
+            m_d.copy_((torch.rand(T, generator=gt, device=DEV) > 0.2).to(torch.uint8))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
