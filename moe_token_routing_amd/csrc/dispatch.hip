@@ -18,10 +18,11 @@
 //             chunk are matched with ballots over the id bits, so the rank
 //             of a slot is the number of earlier slots with its id: the order
 //             within an expert is ascending slot index.
-// When the tile histograms are small (tiles^2 * E below kFuseLimit, every
-// shape up to tens of thousands of slots), step 2 is folded into step 3:
-// each place block sums the histograms itself -- its own exclusive prefix
-// over the tiles and every expert's total -- which saves a launch. With one
+// When the tile histograms are small (tiles^2 * E at most kFuseLimit: up to
+// tens of thousands of slots over a few hundred experts), step 2 is folded
+// into step 3: each place block sums the histograms itself -- its own
+// exclusive prefix over the tiles and every expert's total -- which saves a
+// launch. With one
 // tile (up to 1024 slots) step 1 goes too: the place block's per-wave
 // histograms are the only ones, and their sums are the totals.
 #include <cmath>
@@ -34,7 +35,10 @@ namespace {
 constexpr int kDispBlock = 256;
 constexpr int kDispWaves = kDispBlock / kWave;
 constexpr int kMaxTiles = 256;
-constexpr long long kFuseLimit = 1ll << 22;   // tiles * tiles * E read by the fused place step
+// tiles * tiles * E read by the fused place step: 64 tiles of 256 experts
+// (8192 tokens, top-8) stay fused (13 us against 16 us unfused); 32 tiles
+// of 2560 experts take the separate scan (19 us against 28 us fused)
+constexpr long long kFuseLimit = 1ll << 21;
 constexpr int kHistBatch = 32;                // tile histograms loaded before they are added
 constexpr int kIdBatch = 16;                  // ids per thread loaded before they are counted
 constexpr int kIdChunks = 16;                 // 64-slot chunks of a wave's quarter held in registers
