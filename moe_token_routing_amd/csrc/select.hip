@@ -185,6 +185,8 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
         }
         return;
     }
+    // full lanes of a valid token: every expert of the lane is a candidate
+    if constexpr (FULL) live = (1u << EPL) - 1u;
 
     int my_id = -1;
     float my_l = 0.f;
