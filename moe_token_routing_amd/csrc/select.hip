@@ -57,6 +57,11 @@ __device__ __forceinline__ float sigmoid_rn(float l) {
 constexpr int kSplitBatch = 8;   // split partials loaded before they are added
 constexpr int kLdsBatch = 8;     // a lane's experts loaded (or scanned) at once by select_lds_kernel
 
+// value of lane `src` (wave-uniform) of v: v_readlane_b32, no LDS round trip
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 // One round's winner given this lane's best remaining candidate (has, bk, be):
 // the largest key, and among equal keys the lowest expert id.
 __device__ __forceinline__ uint32_t round_winner(bool has, uint32_t bk, uint32_t be) {
@@ -71,7 +76,7 @@ __device__ __forceinline__ void write_picks(int lane, int k, int my_id, float my
     const float my_s = lane < k ? sigmoid_rn(my_l) : 0.f;
     float total = 0.f;
 #pragma unroll 1
-    for (int j = 0; j < k; ++j) total += __shfl(my_s, j, kWave);
+    for (int j = 0; j < k; ++j) total += lane_value(my_s, j);
     if (lane < k) {
         ids[lane] = my_id;
         w[lane] = my_s / total;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
             }
             const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(e0 + bi));
             const int owner = static_cast<int>(win / EPL);
-            const float l_win = __shfl(bl, owner, kWave);
+            const float l_win = lane_value(bl, owner);
             if (lane == owner) live &= ~(1u << bi);
             if (lane == j) {
                 my_id = static_cast<int>(win);
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
         const float bl = bi >= 0 ? lgs[lane + kWave * bi] : 0.f;
         const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(lane + kWave * bi));
         const int owner = static_cast<int>(win & (kWave - 1));
-        const float l_win = __shfl(bl, owner, kWave);
+        const float l_win = lane_value(bl, owner);
         if (lane == owner) live &= ~(1ull << bi);
         if (lane == j) {
             my_id = static_cast<int>(win);
