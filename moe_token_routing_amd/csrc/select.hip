@@ -312,9 +312,12 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     write_picks(lane, k, my_id, my_l, ids, w);
 }
 
-// Any E: each wave stages its token's keys and logits in its own LDS region
-// (dynamic LDS: kSelectWaves * E * 8 bytes). A lane only touches the entries
-// of its own experts, so no barrier is needed.
+// Any E: each wave stages its token's keys in its own LDS region (dynamic
+// LDS: kSelectWaves * E * 4 bytes). A lane only touches the entries of its
+// own experts, so no barrier is needed. The picks' logits are read back from
+// the token's logit row at the end (the caller's logits, or the row this
+// wave has just written), which keeps the LDS per block at one key per
+// expert and lets four blocks share a CU at 2560 experts.
 __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
@@ -324,8 +327,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     const int wave = threadIdx.x / kWave;
     const int t = blockIdx.x * kSelectWaves + wave;
     if (t >= T) return;
-    uint32_t* keys = sel_lds + static_cast<size_t>(wave) * 2 * E;
-    float* lgs = reinterpret_cast<float*>(keys + E);
+    uint32_t* keys = sel_lds + static_cast<size_t>(wave) * E;
     const size_t plane = static_cast<size_t>(T) * E;
     const bool valid = token_mask[t] != 0;
     // the lane's experts e = lane + 64 i, kLdsBatch at a time: their logits
@@ -362,10 +364,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
 #pragma unroll
         for (int u = 0; u < kLdsBatch; ++u) {
             const int e = e0 + u * kWave;
-            if (e < E) {
-                lgs[e] = l[u];
-                keys[e] = valid ? ordered_key(sigmoid_rn(l[u]) + bias[e]) : 0u;
-            }
+            if (e < E) keys[e] = valid ? ordered_key(sigmoid_rn(l[u]) + bias[e]) : 0u;
         }
     }
     int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
@@ -381,7 +380,6 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     uint64_t live = nloc >= 64 ? ~0ull : ((1ull << nloc) - 1);
 
     int my_id = -1;
-    float my_l = 0.f;
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
         uint32_t bk = 0u;
@@ -402,16 +400,15 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
                 bi = take ? i : bi;
             }
         }
-        const float bl = bi >= 0 ? lgs[lane + kWave * bi] : 0.f;
         const uint32_t win = round_winner(bi >= 0, bk, static_cast<uint32_t>(lane + kWave * bi));
         const int owner = static_cast<int>(win & (kWave - 1));
-        const float l_win = lane_value(bl, owner);
-        if (lane == owner) live &= ~(1ull << bi);
-        if (lane == j) {
-            my_id = static_cast<int>(win);
-            my_l = l_win;
-        }
+        if (lane == owner) live &= ~(1ull << (win / kWave));
+        if (lane == j) my_id = static_cast<int>(win);
     }
+    // lane j < k reads pick j's logit from the row (written above by the
+    // lane that owns the expert, so the wave's stores are made visible first)
+    __threadfence_block();
+    const float my_l = lane < k ? logits[static_cast<size_t>(t) * E + my_id] : 0.f;
     write_picks(lane, k, my_id, my_l, ids, w);
 }
 
@@ -454,7 +451,7 @@ int run_select(const float* partials, int nsplit, float scale, int logits_in, co
     if (epl <= 2) return launch_select_reg<2>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
     if (epl <= 4) return launch_select_reg<4>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
     if (epl <= 8) return launch_select_reg<8>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
-    const size_t lds = static_cast<size_t>(kSelectWaves) * 2 * E * sizeof(uint32_t);
+    const size_t lds = static_cast<size_t>(kSelectWaves) * E * sizeof(uint32_t);
     return launch(select_lds_kernel, dim3(ceil_div(T, kSelectWaves)), dim3(kSelectBlock), lds, stream,
                   partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w);
 }
