@@ -1,4 +1,5 @@
 // Host-side helpers of the library: status strings and cached device facts.
+#include <atomic>
 #include <functional>
 #include <mutex>
 #include <unordered_map>
@@ -9,16 +10,18 @@ namespace moe {
 
 int device_cu_count() {
     constexpr int kMaxDevices = 64;
-    static int cached[kMaxDevices] = {0};
+    // zero until first queried; threads that race on the first query all
+    // store the same value (relaxed atomics: no data race)
+    static std::atomic<int> cached[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;   // benign race: every thread writes the same value
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 int resident_blocks_impl(const void* kernel, int block, size_t lds) {
