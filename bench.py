@@ -41,7 +41,8 @@ Alongside the throughput the line carries:
                 the act-fusion GEMM page, against the FP16 MFMA peak
   expert_fc1_swiglu  the SwiGLU form (moe_expert_fc1_swiglu_nvfp4) over the
                 same 2688 weight rows as gate and up halves
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
+                on the host cores this job may use, and on one core
 """
 from __future__ import annotations
 
@@ -97,29 +98,92 @@ def measured_traffic(workload: str):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(w, sample_tokens: int):
+def host_cores() -> int:
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS
+    when that is set (the share of the host a one-GPU job is given)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
+
+
+_CPU = {}   # the CPU baseline's inputs, set before its worker processes fork
+
+
+def _cpu_route(rows):
+    import oracle as O
+    c = _CPU
+    _, _, ids, tw = O.route(c["hidden"][rows], c["W"], c["bias"], c["mask"][rows], c["k"])
+    return ids, tw
+
+
+def _cpu_norm_quant(rows):
+    import oracle as O
+    c = _CPU
+    return O.norm_quant_nvfp4(c["x"][rows], c["qw"], c["qgc"], c["eps"], np.float32(1.0))
+
+
+def _cpu_combine(rows):
+    import oracle as O
+    c = _CPU
+    return O.combine(c["eo"], c["dest"][rows], c["tw"][rows], c["cg"], 0.0, c["eps"])[0]   # the output rows
+
+
+def cpu_baseline(w, sample_tokens: int, workers: int):
     """The oracle, as it stands, over the first `sample_tokens` tokens of the
-    workload treated as one batch (route -> dispatch -> norm+quant ->
-    combine), with BLAS held to one thread."""
+    workload treated as one batch: route, dispatch, norm + quant, combine.
+    With workers > 1 the per-token steps (route, norm + quant, combine) run on
+    token chunks in that many forked processes and the dispatch, which sees
+    every token, runs in the parent; BLAS is held to one thread per process.
+    Call it before the GPU is initialised (it forks)."""
+    import multiprocessing as mp
+
     import oracle as O
     import workloads as wl
     from threadpoolctl import threadpool_limits
 
     S = min(sample_tokens, w.T)
-    hidden = wl.hidden(w, S)
-    W, bias, mask = wl.router_weight(w), wl.bias(w), wl.token_mask(w, S)
-    x, qw, cg = wl.quant_input(w, S), wl.quant_gain(w), wl.combine_gain(w)
-    eo = wl.expert_out(w, S * w.k)
-    gs = np.float32(1.0)
+    _CPU.clear()
+    _CPU.update(hidden=wl.hidden(w, S), W=wl.router_weight(w), bias=wl.bias(w), mask=wl.token_mask(w, S),
+                k=w.k, x=wl.quant_input(w, S), qw=wl.quant_gain(w), qgc=w.quant_gain_center, eps=w.eps,
+                cg=wl.combine_gain(w), eo=wl.expert_out(w, S * w.k))
+    chunk = -(-S // max(1, workers))
+    parts = [slice(a, min(S, a + chunk)) for a in range(0, S, chunk)]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        _, _, ids, tw = O.route(hidden, W, bias, mask, w.k)
-        _, _, _, dest = O.dispatch(ids, w.E)
-        O.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs)
-        O.combine(eo, dest.reshape(S, w.k), tw, cg, 0.0, w.eps)
+        if workers > 1:
+            pool = mp.get_context("fork").Pool(workers)
+            try:
+                r = pool.map(_cpu_route, parts)
+                ids = np.concatenate([a for a, _ in r])
+                _CPU["tw"] = np.concatenate([b for _, b in r])
+                nq = pool.map_async(_cpu_norm_quant, parts)
+                _, _, _, dest = O.dispatch(ids, w.E)
+                nq.get()
+                pool.close()
+                pool.join()
+                # the combine needs dest: fork a new pool that sees it
+                _CPU["dest"] = dest.reshape(S, w.k)
+                pool = mp.get_context("fork").Pool(workers)
+                pool.map(_cpu_combine, parts)
+            finally:
+                pool.close()
+                pool.join()
+        else:
+            ids, _CPU["tw"] = _cpu_route(slice(0, S))
+            _, _, _, dest = O.dispatch(ids, w.E)
+            _CPU["dest"] = dest.reshape(S, w.k)
+            _cpu_norm_quant(slice(0, S))
+            _cpu_combine(slice(0, S))
         dt = time.perf_counter() - t0
-    return {"value": S / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d tokens of the %s workload as one batch, all four steps, %.1f s" % (S, w.name, dt)}
+    _CPU.clear()
+    how = ("route, norm + quant and combine on token chunks in %d processes, dispatch serial" % workers
+           if workers > 1 else "one process, one thread")
+    return {"value": round(S / dt, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": "first %d tokens of the %s workload as one batch, all four steps, %.1f s; %s"
+                      % (S, w.name, dt, how)}
 
 
 def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10, swiglu: bool = False):
@@ -193,9 +257,20 @@ def main():
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    import workloads as wl
+
+    # the CPU oracle first: its worker processes fork, which must happen
+    # before anything initialises the GPU
+    cpu = None
+    if args.cpu_sample > 0:
+        cores = host_cores()
+        cpu = cpu_baseline(wl.WORKLOADS[args.workload], args.cpu_sample, cores)
+        # one core takes ~5x longer per token: a quarter of the sample
+        cpu["one_core"] = (cpu_baseline(wl.WORKLOADS[args.workload], max(1, args.cpu_sample // 4), 1)
+                           if cores > 1 else None)
+
     import torch
     import moe_token_routing_amd as m
-    import workloads as wl
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -473,8 +548,8 @@ def main():
                      "traffic": measured_traffic(w.name)},
         "cpu_baseline": None,
     }
-    if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result))
 
 

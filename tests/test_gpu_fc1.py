@@ -261,3 +261,88 @@ def test_fc1_swiglu_full_workload_sampled():
     nset, nmis = _check(got_p[rows[perm2]], got_s[rows[perm2]], ref_p, ref_s, near, "fc1 swiglu wide_k")
     assert int(offsets[-1]) == T * k
     print("wide_k sampled rows %d: boundary blocks %d of %d, mismatches inside %d" % (len(rows), nset, near.size, nmis))
+
+
+def test_fc1_scale_bytes_full_range():
+    """Input and weight scale bytes over the whole finite E4M3 range: zero
+    blocks (0x00), every subnormal (0x01-0x07), normals up to 448 (0x7E),
+    drawn uniformly; whole rows of zero scales and of 0x7E too."""
+    g = np.random.default_rng(77)
+    T, k, E, K, N = 64, 4, 8, 256, 256
+    xp = g.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
+    xs = g.integers(0, 0x7F, size=(T, K // 16), dtype=np.uint8)
+    xs[3] = 0x00                      # a token whose every block is zero
+    xs[4] = 0x7E                      # every block at the largest scale
+    xs[5] = g.integers(0, 8, size=K // 16)   # zero and subnormal scales only
+    wp = g.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = g.integers(0, 0x7F, size=(E, N, K // 16), dtype=np.uint8)
+    ws[1, :7] = 0x00
+    ws[2, 7:20] = 0x7E
+    ws[3, 20:40] = g.integers(1, 8, size=(20, K // 16))
+    gw = g.uniform(0.5, 8.0, size=E).astype(np.float32)
+    perm, offsets = _routing(g, T, k, E, invalid=0.05)
+    gx = np.float32(3.0)
+    acc, _ = O.fc1_exact(xp, xs, gx, perm, offsets, k, wp, ws, gw)
+    gy = O.global_scale(O.relu2(acc))
+    args = (xp, xs, gx, perm, offsets, k, wp, ws, gw, gy)
+    got_p, got_s = _run(*args, "scale bytes full range")
+    ref_p, ref_s = O.expert_fc1_nvfp4(*args)
+    near = O.fc1_boundary_blocks(*args)
+    nset, nmis = _check(got_p, got_s, ref_p, ref_s, near, "fc1 scale range")
+    used = int(offsets[-1])
+    assert not got_p[used:].any() and not got_s[used:].any()
+    assert (ref_s[:used] == 0x7E).any() and (ref_s[:used] == 0).any()
+    print("boundary blocks %d of %d, code mismatches inside %d" % (nset, near.size, nmis))
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_fc1_fed_by_the_pre_expert_quantiser(swiglu):
+    """The chain the pages describe: moe_norm_quant_nvfp4's output, grouped
+    by moe_dispatch of the routed ids, fed to the expert FC1 (TensorRT-LLM PR
+    #21842, description; vLLM prepare_trtllm_nvfp4). The quantiser's scales
+    here reach 448 (the static global scale puts the largest block there),
+    E4M3 subnormals (a row of tiny values) and zero (an all-zero row). The
+    quantiser is held to its rule against the oracle, and the FC1 to its rule
+    on exactly the bytes the quantiser emitted."""
+    require_gpu()
+    g = np.random.default_rng(78)
+    T, k, E, K, N = 96, 3, 6, 512, 256
+    x = wl.f32_to_bf16_bits((g.standard_normal((T, K)) * 2).astype(np.float32))
+    x[7] = 0                                                        # zero blocks
+    x[8] = wl.f32_to_bf16_bits((g.standard_normal(K) * 1e-3).astype(np.float32))
+    x[8, :16] = wl.f32_to_bf16_bits(np.full(16, 30.0, np.float32))  # one large block, the rest tiny
+    x[9, 5] = wl.f32_to_bf16_bits(np.float32(400.0))                 # an outlier
+    nw = g.uniform(-0.5, 0.5, K).astype(np.float32)
+    gx = O.global_scale(O.rmsnorm_bf16(x, nw, 1.0, 1e-6))
+    note("fc1 chain: norm_quant T=%d K=%d" % (T, K))
+    xp_d, xs_d = m.norm_quant_nvfp4(dev(x), dev(nw), 1.0, 1e-6, scalar_dev(gx))
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[g.uniform(size=T) < 0.1] = -1                               # invalid tokens
+    counts_d, offsets_d, perm_d, dest_d = m.dispatch(dev(ids), E)
+    torch.cuda.synchronize()
+    xp, xs = host(xp_d), host(xs_d)
+    perm, offsets = host(perm_d), host(offsets_d)
+    # the quantiser against its rule, the dispatch bit for bit
+    from gpu_helpers import check_nvfp4
+    check_nvfp4(x, nw, 1.0, 1e-6, gx, xp, xs, "chain quantiser")
+    for got, want in zip((host(counts_d), offsets, perm, host(dest_d)), O.dispatch(ids, E)):
+        np.testing.assert_array_equal(got, want)
+    assert (xs == 0x7E).any() and (xs == 0).any() and ((xs > 0) & (xs < 8)).any()
+    rows = 2 * N if swiglu else N
+    wp = g.integers(0, 256, size=(E, rows, K // 2), dtype=np.uint8)
+    ws = g.integers(0x30, 0x48, size=(E, rows, K // 16), dtype=np.uint8)
+    gw = g.uniform(1.0, 4.0, size=E).astype(np.float32)
+    fc1 = O.expert_fc1_swiglu_nvfp4 if swiglu else O.expert_fc1_nvfp4
+    near_fn = O.fc1_swiglu_boundary_blocks if swiglu else O.fc1_boundary_blocks
+    acc, _ = O.fc1_exact(xp, xs, gx, perm, offsets, k, wp, ws, gw)
+    act = O.swiglu(acc[:, :N], acc[:, N:]) if swiglu else O.relu2(acc)
+    gy = O.global_scale(act)
+    note("fc1 chain: fc1 swiglu=%s" % swiglu)
+    call = m.expert_fc1_swiglu_nvfp4 if swiglu else m.expert_fc1_nvfp4
+    yp_d, ys_d = call(xp_d, xs_d, scalar_dev(gx), perm_d, offsets_d, k, dev(wp), dev(ws), dev(gw), scalar_dev(gy))
+    torch.cuda.synchronize()
+    args = (xp, xs, gx, perm, offsets, k, wp, ws, gw, gy)
+    ref_p, ref_s = fc1(*args)
+    near = near_fn(*args)
+    nset, nmis = _check(host(yp_d), host(ys_d), ref_p, ref_s, near, "fc1 chain")
+    print("chain swiglu=%s: boundary blocks %d of %d, mismatches inside %d" % (swiglu, nset, near.size, nmis))

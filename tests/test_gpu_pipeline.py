@@ -1,13 +1,23 @@
 """The four calls chained on one stream at the full prefill shape (the
 benchmark's workload and launch configuration), checked end to end against
-the oracle on sampled tokens, and replayed inside a HIP graph."""
+the oracle on every token, and replayed inside a HIP graph -- on one stream
+and with norm + quant forked onto a second stream -- with every replay
+checked against the oracle and against an eager run.
+
+TensorRT-LLM PR #21356, "Add the Muse Spark Open decoder fast paths": the
+expert input is prepared on an auxiliary stream beside the routing ("Where
+they plug in"), and each fused path is tested against the reference
+composition and under CUDA graph replay with changed inputs (Test Coverage).
+"""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
+import route_checks as RC
 import workloads as wl
-from gpu_helpers import DEV, assert_bf16_within, dev, host, note, require_gpu, scalar_dev
+from gpu_helpers import (DEV, check_combine, check_nvfp4, dev, host, note, require_gpu,
+                         scalar_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,33 +44,36 @@ def _pipeline(d, gs):
                 perm=host(perm), dest=host(dest), packed=host(packed), scales=host(scales), out=host(out))
 
 
+def _check_step(r, hidden, W, bias, mask, k, E, x, qw, qgc, eps, gs, eo, cg, route_rows, other_rows, what):
+    """One step's outputs against the oracle: R1 on every token, R2 on
+    route_rows, dispatch bit-exact, the NVFP4 and combine rules on
+    other_rows (None: every row)."""
+    T = mask.shape[0]
+    ids_o, w_o = O.route_from_logits(r["lg"], bias, mask, k)
+    np.testing.assert_array_equal(r["ids"], ids_o, err_msg=what + ": R1 ids")
+    assert (np.abs(r["tw"].astype(np.float64) - w_o) <= 1e-5 * np.abs(w_o)).all(), what + ": R1 weights"
+    lg_ref, mag = O.router_logits(hidden[route_rows], W)
+    RC.assert_r2(r["lg"][route_rows], lg_ref, mag, mask[route_rows] != 0, what)
+    for k_, rv in zip(("counts", "offsets", "perm", "dest"), O.dispatch(r["ids"], E)):
+        np.testing.assert_array_equal(r[k_], rv, err_msg=what + ": dispatch " + k_)
+    assert r["offsets"][-1] == int((mask != 0).sum()) * k
+    rows = np.arange(T) if other_rows is None else other_rows
+    check_nvfp4(x[rows], qw, qgc, eps, gs, r["packed"][rows], r["scales"][rows], what + ": nvfp4")
+    slots = r["dest"].reshape(T, k)
+    check_combine(eo, slots[rows], r["tw"][rows], cg, 0.0, eps, r["out"][rows], what + ": combine")
+
+
 @pytest.mark.parametrize("name,T", [("prefill", None), ("wide_k", 4096)])
 def test_pipeline_end_to_end(name, T):
+    """Every token: R1, R2, dispatch, NVFP4 and combine against the oracle."""
     require_gpu()
     d = _inputs(name, T)
     w, T = d["w"], d["T"]
-    g = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([g.choice(T, 256, replace=False), [0, T - 1]]))
-    gs = O.global_scale(O.rmsnorm_bf16(d["x"][rows], d["qw"], w.quant_gain_center, w.eps))
+    gs = O.global_scale(O.rmsnorm_bf16(d["x"], d["qw"], w.quant_gain_center, w.eps))
     note("pipeline %s T=%d" % (name, T))
     r = _pipeline(d, gs)
-    # route: the oracle's routing of the GPU logits (every token)
-    ids_o, w_o = O.route_from_logits(r["lg"], d["bias"], d["mask"], w.k)
-    np.testing.assert_array_equal(r["ids"], ids_o)
-    assert (np.abs(r["tw"].astype(np.float64) - w_o) <= 1e-5 * np.abs(w_o)).all()
-    # dispatch of those ids (every slot)
-    ref = O.dispatch(r["ids"], w.E)
-    for k_, rv in zip(("counts", "offsets", "perm", "dest"), ref):
-        np.testing.assert_array_equal(r[k_], rv, err_msg=k_)
-    assert r["offsets"][-1] == int(d["mask"].sum()) * w.k
-    # combine through dest (sampled tokens)
-    slots = r["dest"].reshape(T, w.k)
-    ref_out, mag = O.combine(d["eo"], slots[rows], r["tw"][rows], d["cg"], 0.0, w.eps)
-    assert_bf16_within(r["out"][rows], ref_out, mag, 2.0, "pipeline combine")
-    # quant (sampled rows, outside the stated set)
-    rp, rs = O.norm_quant_nvfp4(d["x"][rows], d["qw"], w.quant_gain_center, w.eps, gs)
-    near = O.midpoint_boundary_blocks(d["x"][rows], d["qw"], w.quant_gain_center, w.eps)
-    assert np.array_equal(r["scales"][rows][~near], rs[~near])
+    _check_step(r, d["hidden"], d["W"], d["bias"], d["mask"], w.k, w.E, d["x"], d["qw"], w.quant_gain_center,
+                w.eps, gs, d["eo"], d["cg"], np.arange(T), None, "pipeline %s" % name)
 
 
 @pytest.mark.parametrize("name", ["decode", "prefill"])
@@ -69,7 +82,10 @@ def test_pipeline_graph_replay(name, two_stream):
     """Capture the four calls in a HIP graph -- on one stream, or with norm +
     quant forked onto a second stream beside route -> dispatch -> combine --
     and replay it with new inputs copied into the captured buffers; every
-    replay must equal a serial eager run bit for bit. At 128 tokens and at
+    replay must equal a serial eager run bit for bit and meet the parity
+    rules against the oracle (R1, dispatch on every token; R2, NVFP4 and
+    combine on every token at 128 tokens, on 258 sampled tokens at 8192).
+    At 128 tokens and at
     the 8192-token prefill batch, whose calls take their large-batch forms
     (weight planes split by a kernel of their own, tile histograms summed in
     the place step, norm + quant copying rows ahead, one block per token in
@@ -151,3 +167,13 @@ def test_pipeline_graph_replay(name, two_stream):
         eager = snapshot()
         for a, b in zip(replayed, eager):
             np.testing.assert_array_equal(a, b)
+        # and the replay against the oracle on the inputs it was given
+        r = dict(zip(("lg", "ids", "tw", "counts", "offsets", "perm", "dest", "packed", "scales", "out"), replayed))
+        hidden_h, x_h, mask_h = host(h_d), host(x_d), host(m_d)
+        if name == "decode":
+            route_rows, other_rows = np.arange(T), None
+        else:
+            route_rows = other_rows = np.unique(np.concatenate([g.choice(T, 256, replace=False), [0, T - 1]]))
+        _check_step(r, hidden_h, d["W"], d["bias"], mask_h, w.k, w.E, x_h, d["qw"], 1.0, w.eps, np.float32(0.5),
+                    d["eo"], d["cg"], route_rows, other_rows,
+                    "graph replay %s %d two_stream=%s" % (name, rep, two_stream))

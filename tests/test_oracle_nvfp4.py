@@ -169,3 +169,70 @@ def test_rank_block_quant_matches_contiguous():
         pooled = np.concatenate([x[:, r * S:(r + 1) * S] for r in range(tp)], axis=0)
         got = O.norm_quant_nvfp4_rank_block(pooled, M, nw, w.quant_gain_center, w.eps, gs)
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def _step_order_blocks():
+    """The RESULT lines of golden/nvfp4_step_order.txt: hand-checkable blocks
+    (every FP32 rounding written out in exact arithmetic) whose scale byte or
+    codes depend on the order of the quantiser's steps (vLLM
+    prepare_trtllm_nvfp4, _quantize_nvfp4_global_scale)."""
+    out = []
+    with open(os.path.join(GOLDEN, "nvfp4_step_order.txt")) as f:
+        for line in f:
+            if not line.startswith("RESULT "):
+                continue
+            fields = dict(kv.split("=") for kv in line.split()[2:])
+            gs = np.array([int(fields["gs"], 16)], np.uint32).view(np.float32)[0]
+            y = np.array([int(b, 16) for b in fields["y"].split(",")], np.uint16)
+            scale = int(fields["scale"], 16)
+            packed = np.array([int(b, 16) for b in fields["packed"].split(",")], np.uint8)
+            out.append((line.split()[1], gs, y, scale, packed))
+    return out
+
+
+def test_step_order_golden_blocks():
+    blocks = _step_order_blocks()
+    assert len(blocks) == 5
+    for name, gs, y, scale, packed in blocks:
+        yv = O.bf16_bits_to_f64(y).astype(np.float32)[None, :]
+        p, s = O.nvfp4_quantize(yv, gs)
+        assert int(s[0, 0]) == scale, name
+        np.testing.assert_array_equal(p[0], packed, err_msg=name)
+
+
+def _reordered_quantize(y, gs, order):
+    """A deliberately reordered quantiser (numpy FP32), to show that the
+    golden blocks tell the printed order from its plausible rearrangements."""
+    F = np.float32
+    y = np.asarray(y, np.float32)
+    amax = np.max(np.abs(y))
+    if order == "gs_amax_first":
+        s = (F(gs) * amax) * (F(1) / F(6))
+    else:
+        s = F(gs) * (amax * (F(1) / F(6)))
+    sf = O.e4m3_encode_satfinite(np.array([s], np.float32))
+    sfv = O.e4m3_decode(sf).astype(np.float32)[0]
+    if sfv == 0:
+        out = F(0)
+    elif order == "gs_over_sf":
+        out = F(gs) / sfv
+    elif order == "rcp_of_sf_over_gs":
+        out = F(1) / (sfv / F(gs))
+    else:
+        out = F(1) / (sfv * (F(1) / F(gs)))
+    codes = O.e2m1_encode(y * out)
+    return codes[0::2] | (codes[1::2] << 4), int(sf[0])
+
+
+@pytest.mark.parametrize("order", ["gs_amax_first", "gs_over_sf", "rcp_of_sf_over_gs"])
+def test_step_order_golden_rejects_reordered_chains(order):
+    blocks = _step_order_blocks()
+    printed_ok = all(
+        (lambda r: r[1] == scale and np.array_equal(r[0], packed))(
+            _reordered_quantize(O.bf16_bits_to_f64(y), gs, "printed"))
+        for _, gs, y, scale, packed in blocks)
+    assert printed_ok
+    mismatched = [name for name, gs, y, scale, packed in blocks
+                  if (lambda r: r[1] != scale or not np.array_equal(r[0], packed))(
+                      _reordered_quantize(O.bf16_bits_to_f64(y), gs, order))]
+    assert mismatched, order + " passes every golden block"
