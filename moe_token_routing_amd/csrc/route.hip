@@ -47,6 +47,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTargetBlocks = 480;   // about two blocks per CU
+constexpr int kPipeTargetBlocks = 256;   // one block per CU (proj_pipe_kernel)
 
 // ---------------------------------------------------------------- split ----
 
@@ -333,6 +334,151 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
         }
 }
 
+// ------------------------------------------------------ pipelined gemm ----
+
+// The projection for large batches (BF16 input, weights split by
+// split_weight_kernel), software-pipelined so that no step waits for a load
+// issued in the previous one.
+//
+// Block tile: 256 tokens x 256 experts, eight waves side by side along the
+// experts, each 256 x 32 (eight v_mfma_f32_32x32x16_bf16 accumulators); one
+// block per CU (two waves per SIMD). Per block, a 256-token tile reads each
+// weight fragment once for twice as many tokens as a 128-token tile, which
+// halves the L2 -> CU weight traffic.
+//
+// Pipeline: every K-step s issues one group of loads for step s + kLook -- one
+// direct-to-LDS 16-byte load of the input stage per wave (the eight waves
+// fill the 8 KB stage of 256 rows x 16 columns) and the wave's three 16-byte
+// weight fragments (one per BF16 plane) into one of kLook + 1 register sets.
+// Loads complete in issue order, so waiting until at most (kLook - 1) groups
+// are outstanding (s_waitcnt vmcnt) means step s's group has landed while
+// the next kLook - 1 stay in flight; a barrier without a memory fence then
+// makes every wave's part of the input stage visible. The LDS ring has
+// kLook + 1 stages: the stage refilled at step s is the one all waves finished
+// reading before that barrier. The loop is unrolled over the register sets
+// and nothing is issued conditionally inside it (loads past the last step
+// repeat the last step's addresses into a set and a stage nobody reads), so
+// the compiler's own wait placement stays exact.
+constexpr int kPipeWaves = 8;
+constexpr int kPipeBlock = kPipeWaves * kWave;
+constexpr int kPipeMT = 8;                       // 32-token row groups per wave
+constexpr int kPipeBM = 32 * kPipeMT;            // 256 tokens
+constexpr int kPipeBN = 32 * kPipeWaves;         // 256 experts
+constexpr int kLook = 3;                         // steps of loads in flight
+constexpr int kPipeSets = kLook + 1;             // register sets = LDS stages
+constexpr int kPipeStage = kPipeBM * 32;         // 8 KB: 256 rows x 16 BF16
+constexpr int kPipeLoads = 4;                    // loads per wave and step
+constexpr size_t kPipeLds = static_cast<size_t>(kPipeSets) * kPipeStage;
+static_assert(kPipeBM * 2 / kWave == kPipeWaves, "one input load per wave and step");
+static_assert(kPipeSets == 4, "the main loop is unrolled over four sets");
+
+// s_waitcnt with only the vector-memory count constrained (expcnt and
+// lgkmcnt at their maxima), for gfx9's split vmcnt field.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Block b works on K-slice b % nsplit (each XCD keeps one slice of the
+// weight planes in its L2 when nsplit divides 8) and token tile b / nsplit;
+// the expert tile is tile / tiles_m. Requires (kend - kbeg) to be a positive
+// multiple of 64 for every slice (plan_route checks it).
+__global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2))) void proj_pipe_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w_frags, int T, int H, int E, int kslice,
+    int nsplit, int tiles_m, float* __restrict__ partials) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int split = blockIdx.x % nsplit;
+    const int tile = blockIdx.x / nsplit;
+    const int m0 = (tile % tiles_m) * kPipeBM;
+    const int n_tile = tile / tiles_m;
+    const int kbeg = split * kslice;
+    const int nst = (min(H, kbeg + kslice) - kbeg) / kKC;
+
+    f32x16_t acc[kPipeMT];
+#pragma unroll
+    for (int mt = 0; mt < kPipeMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+
+    // this wave's input load: rows 32 wave + lane / 2 of the tile, chunk
+    // (lane & 1) ^ swz(row) of the stage's 16 columns (rows past T read row
+    // T - 1, whose results are never stored)
+    const int a_row = wave * 32 + (lane >> 1);
+    const int a_chunk = (lane & 1) ^ swz(a_row);
+    const uint16_t* a_src = a + static_cast<size_t>(min(m0 + a_row, T - 1)) * H + kbeg + a_chunk * 8;
+    char* a_dst = lds + wave * 1024;
+    // this wave's weight fragments: group `wave` of the tile's run for each
+    // K-step (3 planes x 8 groups x 64 lanes of 16 bytes)
+    constexpr int G = kPipeBN / 32;
+    const bf16x8_t* b_src = reinterpret_cast<const bf16x8_t*>(w_frags) +
+                            (static_cast<size_t>(n_tile) * (H / kKC) + kbeg / kKC) * (3 * G * kWave) +
+                            wave * kWave + lane;
+    bf16x8_t bq[kPipeSets][3];
+    // The blocks of one XCD run the same K-slice in step: each starts its walk
+    // over the slice at an offset of its own (two K-steps per token tile) so
+    // that at any moment they read different lines of the shared weight
+    // planes instead of the same few (-7% at 8192 tokens). The order of a
+    // block's additions is fixed, so results stay reproducible.
+    const int rot = ((tile % tiles_m) * 2) % max(nst, 1);
+
+    auto issue = [&](int step, int set) {
+        const int s = step + rot < nst ? step + rot : step + rot - nst;
+        __builtin_amdgcn_global_load_lds(a_src + s * kKC, a_dst + set * kPipeStage, 16, 0, 0);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) bq[set][p] = b_src[static_cast<size_t>(s) * (3 * G * kWave) + p * G * kWave];
+    };
+
+    if (nst > 0) {
+#pragma unroll
+        for (int s = 0; s < kLook; ++s) {
+            issue(s, s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int s0 = 0;
+        do {
+#pragma unroll
+            for (int ph = 0; ph < kPipeSets; ++ph) {
+                const int s = s0 + ph;
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<(kLook - 1) * kPipeLoads>();   // step s's loads have landed
+                __builtin_amdgcn_s_barrier();              // ... in every wave
+                __builtin_amdgcn_sched_barrier(0);
+                issue(min(s + kLook, nst - 1), (ph + kLook) % kPipeSets);
+                __builtin_amdgcn_sched_barrier(0);
+                const char* base = lds + ph * kPipeStage;
+                bf16x8_t av[kPipeMT];
+#pragma unroll
+                for (int mt = 0; mt < kPipeMT; ++mt)
+                    av[mt] = *reinterpret_cast<const bf16x8_t*>(base + slot_bytes(mt * 32 + (lane & 31), lane >> 5));
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+#pragma unroll
+                    for (int mt = 0; mt < kPipeMT; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bq[ph][p], acc[mt], 0, 0, 0);
+            }
+            s0 += kPipeSets;
+        } while (s0 < nst);
+        wait_vmcnt<0>();   // the repeated loads of the last steps, before the wave ends
+    }
+
+    // accumulator layout: lane holds expert column (lane & 31) and token rows
+    // 8 (i / 4) + 4 (lane / 32) + (i % 4), i = 0..15
+    float* out = partials + static_cast<size_t>(split) * T * E;
+    const int col = n_tile * kPipeBN + wave * 32 + (lane & 31);
+    if (col < E) {
+#pragma unroll
+        for (int mt = 0; mt < kPipeMT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (row < T) out[static_cast<size_t>(row) * E + col] = acc[mt][i];
+            }
+    }
+}
+
 // From this many tokens the weights are split once per call into
 // fragment-ordered planes; below, each wave splits the FP32 weights it loads.
 constexpr int kPresplitTokens = 4096;
@@ -342,6 +488,7 @@ constexpr int kPresplitTokens = 4096;
 struct RoutePlan {
     int na, mt, nt;                 // kernel variant
     bool presplit;
+    bool pipe;                      // proj_pipe_kernel (256 x 256 tiles) instead of proj_kernel
     int tiles_m, tiles_n, nsplit, kslice;
     size_t w_planes_bytes, a_planes_bytes, partial_bytes;
 };
@@ -366,6 +513,28 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
     p.kslice = per * kKC;
     p.nsplit = ceil_div(H, p.kslice);
     p.presplit = T >= kPresplitTokens;
+    p.pipe = false;
+    // large batches of BF16 input whose K-steps divide into whole unrolled
+    // rounds of four: the pipelined kernel
+    // (one block per CU), when its grid is a whole number of GPU-fulls;
+    // otherwise (a last partial wave of blocks) the two-blocks-per-CU kernel
+    // balances better
+    if (p.presplit && p.na == 1 && H % (4 * kKC) == 0) {
+        const int tm = ceil_div(T, kPipeBM), tn = ceil_div(E, kPipeBN);
+        const int rounds = H / (4 * kKC);           // unrolled rounds of four K-steps
+        int n = 1;
+        while (tm * tn * n < kPipeTargetBlocks && n * 2 <= rounds && n < 64) n *= 2;
+        const int kslice = ceil_div(rounds, n) * 4 * kKC;
+        const int nsplit = ceil_div(H, kslice);
+        if ((tm * tn * nsplit) % kPipeTargetBlocks == 0) {
+            p.pipe = true;
+            p.nt = 2;                               // fragment groups of 256-expert tiles
+            p.tiles_m = tm;
+            p.tiles_n = tn;
+            p.kslice = kslice;
+            p.nsplit = nsplit;
+        }
+    }
     // fragment-ordered planes, padded to whole expert tiles
     p.w_planes_bytes = p.presplit ? round256(static_cast<size_t>(3) * p.tiles_n * 128 * p.nt * H * sizeof(uint16_t)) : 0;
     p.a_planes_bytes = p.na == 3 ? round256(static_cast<size_t>(3) * T * H * sizeof(uint16_t)) : 0;
@@ -387,6 +556,9 @@ int launch_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uin
 
 int run_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uint16_t* w_frags, int T, int H,
              int E, float* partials, void* stream) {
+    if (p.pipe)
+        return launch(proj_pipe_kernel, dim3(p.tiles_m * p.tiles_n * p.nsplit), dim3(kPipeBlock), kPipeLds, stream,
+                      a, w_frags, T, H, E, p.kslice, p.nsplit, p.tiles_m, partials);
 #define MOE_PROJ(NA, MT, NT) \
     if (p.na == NA && p.mt == MT && p.nt == NT) \
         return launch_proj<NA, MT, NT>(p, a, W, w_frags, T, H, E, partials, stream);

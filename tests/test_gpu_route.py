@@ -92,10 +92,12 @@ def test_route_full_size(name):
 
 # Closed-form pins of the FP32 weights, on both weight-split paths (below 4096
 # tokens each wave splits the FP32 weights in registers; from 4096 a kernel
-# splits them into planes first), for BF16 and FP32 input, and at the prefill
-# shape in the benchmark's launch configuration.
+# splits them into planes first), for BF16 and FP32 input, on both projection
+# kernels (128 x 256 tiles, two blocks per CU; 256 x 256 pipelined tiles, one
+# block per CU: 8000 x 960 x 200 ragged, and the prefill shape in the
+# benchmark's launch configuration).
 _PIN_SHAPES = [(300, 1024, 300, "bf16"), (4100, 1024, 300, "bf16"), (300, 1040, 200, "f32"),
-               (4100, 512, 300, "f32"), (8192, 8192, 256, "bf16")]
+               (4100, 512, 300, "f32"), (8000, 960, 200, "bf16"), (8192, 8192, 256, "bf16")]
 
 
 @pytest.mark.parametrize("T,H,E,dtype", _PIN_SHAPES)
@@ -145,9 +147,11 @@ def test_route_scale_and_ragged_shapes():
     # 4096 it reads planes split by a kernel of their own: both with a ragged
     # token tile and a padded expert tile
     # (token tiles of 32, 64 or 128 rows by count: 3000 takes 128-row tiles
-    # with the in-register split)
+    # with the in-register split; 8000 x 960 x 200 takes the pipelined
+    # 256 x 256 tiles: a 64-row last token tile, a padded expert tile and
+    # eight K-slices of 128 columns but the last of 64)
     for T, H, E, k in [(1, 16, 1, 1), (3, 48, 5, 5), (70, 1040, 200, 6), (129, 256, 64, 32), (33, 4096, 4096, 8),
-                       (9, 16384, 64, 4), (3000, 512, 256, 8), (4100, 272, 300, 8)]:
+                       (9, 16384, 64, 4), (3000, 512, 256, 8), (4100, 272, 300, 8), (8000, 960, 200, 8)]:
         note("route ragged T=%d H=%d E=%d k=%d" % (T, H, E, k))
         hidden = wl.f32_to_bf16_bits(g.standard_normal((T, H)).astype(np.float32))
         W = (g.standard_normal((E, H)) * 0.02).astype(np.float32)
