@@ -9,6 +9,8 @@
  *                         per-token validity mask
  *   moe_dispatch          expert histogram, exclusive prefix scan, stable
  *                         permutation of the routed slots by expert
+ *                         (moe_dispatch_noalloc: the same without a workspace,
+ *                         for callers that cannot allocate)
  *   moe_norm_quant_nvfp4  RMSNorm of the expert input with one BF16 rounding,
  *                         fused with NVFP4 quantisation (E2M1 codes, E4M3
  *                         block-16 scales, static global scale); the
@@ -31,7 +33,8 @@
  *     the current HIP device), row-major, contiguous and 16-byte aligned
  *     (MOE_ERR_ALIGN otherwise). The caller owns all
  *     memory; the library never allocates, frees or synchronises, and keeps no
- *     state between calls.
+ *     state between calls (moe_dispatch_noalloc's static device scratch, the
+ *     one exception, is described with it).
  *   - `stream` is the caller's hipStream_t (NULL = the null stream). Work is
  *     enqueued on it; the call returns without waiting.
  *   - The return value is MOE_OK (0) or a negative MOE_ERR_* status. Every
@@ -152,6 +155,29 @@ size_t moe_dispatch_workspace_bytes(int T, int k, int E);
 int moe_dispatch(const int32_t* topk_ids, int T, int k, int E,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch_noalloc — moe_dispatch without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments (minus workspace), outputs, checks and kernels as
+ * moe_dispatch. The per-tile histogram scratch is a static device array of
+ * the library, 4 MiB (256 tiles x MOE_MAX_EXPERTS int32; every shape
+ * moe_dispatch accepts fits), one copy per GPU the library runs on, held
+ * until the process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call there. Nothing is allocated or
+ * freed. Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (each call writes every entry it reads, so nothing needs
+ * clearing): calls that may overlap on one GPU -- on different streams, or
+ * from different host threads without ordering -- race and must not be
+ * issued. A shape needing more scratch than the array would be rejected
+ * with WORKSPACE.
+ * Errors: NULL_ARG, BAD_SHAPE, ALIGN, WORKSPACE, HIP.
+ */
+int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
+                         void* stream);
 
 /*
  * moe_norm_quant_nvfp4 — RMSNorm + NVFP4 quantisation of the expert input.

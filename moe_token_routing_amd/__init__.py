@@ -37,6 +37,7 @@ _SIGNATURES = {
                            _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_dispatch_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_dispatch": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "moe_dispatch_noalloc": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "moe_norm_quant_nvfp4": (_c_int, [_vp, _vp, _c_float, _c_float, _vp, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_norm_quant_nvfp4_rank_block": (_c_int, [_vp, _c_int, _vp, _c_float, _c_float, _vp, _c_int, _c_int,
                                                  _vp, _vp, _vp]),
@@ -183,6 +184,29 @@ def dispatch(topk_ids: torch.Tensor, E: int, *, counts=None, offsets=None, perm=
     _check("moe_dispatch", lib().moe_dispatch(
         _ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(dest),
         _ptr(workspace), ws_len, _stream(dev)))
+    return counts, offsets, perm, dest
+
+
+def dispatch_noalloc(topk_ids: torch.Tensor, E: int, *, counts=None, offsets=None, perm=None, dest=None):
+    """moe_dispatch_noalloc: moe_dispatch with the library's static device
+    scratch instead of a workspace (outputs are allocated here when not
+    given, as in dispatch()). Returns (counts, offsets, perm, dest)."""
+    dev = topk_ids.device
+    _need(topk_ids, "topk_ids", (torch.int32,), None, dev)
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T,k]")
+    T, k = topk_ids.shape
+    n = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm = torch.empty(n, dtype=torch.int32, device=dev) if perm is None else perm
+    dest = torch.empty(n, dtype=torch.int32, device=dev) if dest is None else dest
+    _need(counts, "counts", (torch.int32,), (E,), dev)
+    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    _need(perm, "perm", (torch.int32,), (n,), dev)
+    _need(dest, "dest", (torch.int32,), (n,), dev)
+    _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        _ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(dest), _stream(dev)))
     return counts, offsets, perm, dest
 
 

@@ -25,6 +25,7 @@
 // launch. With one
 // tile (up to 1024 slots) step 1 goes too: the place block's per-wave
 // histograms are the only ones, and their sums are the totals.
+#include <atomic>
 #include <cmath>
 
 #include "launch.hpp"
@@ -323,36 +324,12 @@ __global__ __launch_bounds__(kDispBlock) void zero_kernel(int32_t* __restrict__ 
     }
 }
 
-}  // namespace
-}  // namespace moe
-
-extern "C" size_t moe_dispatch_workspace_bytes(int T, int k, int E) {
-    using namespace moe;
-    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return 0;
-    const long long n = static_cast<long long>(T) * k;
-    if (n == 0) return 0;
+// The launches of one dispatch, given the tile histogram scratch
+// (moe_dispatch_workspace_bytes(T, k, E) bytes; every entry a launch reads
+// is written earlier in the same call, so nothing needs clearing).
+int run_dispatch(const int32_t* topk_ids, long long n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                 int32_t* dest, int32_t* tile_counts, void* stream) {
     const TilePlan p = plan_tiles(n);
-    const size_t bytes = static_cast<size_t>(p.tiles) * E * sizeof(int32_t);
-    return (bytes + 255) / 256 * 256;
-}
-
-extern "C" int moe_dispatch(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
-                            int32_t* offsets, int32_t* perm, int32_t* dest, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-    using namespace moe;
-    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_BAD_SHAPE;
-    const long long n = static_cast<long long>(T) * k;
-    if (n >= (1ll << 31)) return MOE_ERR_BAD_SHAPE;
-    if (!counts || !offsets) return MOE_ERR_NULL_ARG;
-    if (n > 0 && (!topk_ids || !perm || !dest)) return MOE_ERR_NULL_ARG;
-    if (!all_aligned16(topk_ids, counts, offsets, perm, dest)) return MOE_ERR_ALIGN;
-    if (n == 0)   // no slots: counts and offsets are all zero (a kernel, not a memset node)
-        return launch(zero_kernel, dim3(1), dim3(kDispBlock), 0, stream, counts, offsets, E);
-    const size_t need = moe_dispatch_workspace_bytes(T, k, E);
-    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MOE_ERR_ALIGN;
-    const TilePlan p = plan_tiles(n);
-    int32_t* tile_counts = static_cast<int32_t*>(workspace);
     const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) + 1 + static_cast<size_t>(kDispWaves) * E);
     if (p.tiles == 1)   // one tile: the place step counts it itself
         return launch(place_kernel<kPlaceSingle>, dim3(1), dim3(kDispBlock), lds + sizeof(int32_t) * 2 * E,
@@ -370,4 +347,95 @@ extern "C" int moe_dispatch(const int32_t* topk_ids, int T, int k, int E, int32_
     if (rc) return rc;
     return launch(place_kernel<kPlaceScanned>, dim3(p.tiles), dim3(kDispBlock), lds, stream, topk_ids, p.n, E,
                   p.tile, p.tiles, static_cast<const int32_t*>(tile_counts), counts, offsets, perm, dest);
+}
+
+// Argument checks shared by both entry points (before any launch).
+int check_dispatch(const int32_t* topk_ids, int T, int k, int E, const int32_t* counts, const int32_t* offsets,
+                   const int32_t* perm, const int32_t* dest) {
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_BAD_SHAPE;
+    const long long n = static_cast<long long>(T) * k;
+    if (n >= (1ll << 31)) return MOE_ERR_BAD_SHAPE;
+    if (!counts || !offsets) return MOE_ERR_NULL_ARG;
+    if (n > 0 && (!topk_ids || !perm || !dest)) return MOE_ERR_NULL_ARG;
+    if (!all_aligned16(topk_ids, counts, offsets, perm, dest)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+}  // namespace
+
+// Scratch of the allocation-free dispatch: the per-tile expert histograms,
+// at most kMaxTiles x MOE_MAX_EXPERTS int32 (4 MiB), which every supported
+// shape fits. One copy per GPU the library runs on, held until the process
+// ends. Host code never passes this name to a kernel (on the host it is only
+// a handle); it uses the device address hipGetSymbolAddress returns.
+static __device__ __align__(256) int32_t scratch[kMaxTiles * MOE_MAX_EXPERTS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (threads racing on the first lookup store the same address).
+int32_t* scratch_address(int* status) {
+    static std::atomic<int32_t*> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *status = MOE_ERR_HIP;
+        return nullptr;
+    }
+    int32_t* ptr = cached[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+            *status = MOE_ERR_HIP;
+            return nullptr;
+        }
+        ptr = static_cast<int32_t*>(addr);
+        cached[dev].store(ptr, std::memory_order_release);
+    }
+    *status = MOE_OK;
+    return ptr;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_dispatch_workspace_bytes(int T, int k, int E) {
+    using namespace moe;
+    if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    const long long n = static_cast<long long>(T) * k;
+    if (n == 0) return 0;
+    const TilePlan p = plan_tiles(n);
+    const size_t bytes = static_cast<size_t>(p.tiles) * E * sizeof(int32_t);
+    return (bytes + 255) / 256 * 256;
+}
+
+extern "C" int moe_dispatch(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                            int32_t* offsets, int32_t* perm, int32_t* dest, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    const int rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
+    if (rc) return rc;
+    const long long n = static_cast<long long>(T) * k;
+    if (n == 0)   // no slots: counts and offsets are all zero (a kernel, not a memset node)
+        return launch(zero_kernel, dim3(1), dim3(kDispBlock), 0, stream, counts, offsets, E);
+    const size_t need = moe_dispatch_workspace_bytes(T, k, E);
+    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+    return run_dispatch(topk_ids, n, E, counts, offsets, perm, dest, static_cast<int32_t*>(workspace), stream);
+}
+
+extern "C" int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                                    int32_t* offsets, int32_t* perm, int32_t* dest, void* stream) {
+    using namespace moe;
+    const int rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
+    if (rc) return rc;
+    const long long n = static_cast<long long>(T) * k;
+    if (n == 0)
+        return launch(zero_kernel, dim3(1), dim3(kDispBlock), 0, stream, counts, offsets, E);
+    if (moe_dispatch_workspace_bytes(T, k, E) > sizeof(scratch)) return MOE_ERR_WORKSPACE;
+    int status = MOE_OK;
+    int32_t* tile_counts = scratch_address(&status);
+    if (status) return status;
+    return run_dispatch(topk_ids, n, E, counts, offsets, perm, dest, tile_counts, stream);
 }

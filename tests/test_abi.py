@@ -28,7 +28,8 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"moe_status_string", "moe_route_workspace_bytes", "moe_route",
-                          "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_norm_quant_nvfp4",
+                          "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_dispatch_noalloc",
+                          "moe_norm_quant_nvfp4",
                           "moe_norm_quant_nvfp4_rank_block", "moe_combine",
                           "moe_expert_fc1_workspace_bytes", "moe_expert_fc1_nvfp4",
                           "moe_expert_fc1_swiglu_nvfp4"}
@@ -122,6 +123,17 @@ def test_dispatch_rejects_before_launch(lib):
     assert f(FAKE, 4, 2, 16, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     assert f(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -4
     assert f(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -4
+
+
+def test_dispatch_noalloc_rejects_before_launch(lib):
+    f = lib.moe_dispatch_noalloc
+    assert f(FAKE, 4, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert f(FAKE, 4, 33, 64, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert f(FAKE, 4, 2, 4097, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert f(FAKE, -1, 2, 16, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert f(FAKE, 4, 2, 16, None, FAKE, FAKE, FAKE, None) == -1
+    assert f(None, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 4, 2, 16, FAKE, FAKE, V((1 << 20) + 4), FAKE, None) == -7
 
 
 def test_expert_fc1_rejects_before_launch(lib):
