@@ -19,13 +19,15 @@
 //    kernel of its own, into planes in HBM) and the six products with
 //    plane-index sum <= 2 are accumulated (the three dropped ones are below
 //    2^-23 of |h*W|).
-//  * Where the weights are split depends on the token count: from 4096
-//    tokens one kernel per call writes the planes in MFMA fragment order and
-//    each wave loads its fragments with one 16-byte load each; below, each
-//    wave loads the FP32 weights themselves, 8 consecutive K values of one
-//    expert per lane (the B operand's layout), and splits them in registers
-//    (v_cvt_pk_bf16_f32, two values at a time), which saves the split
-//    kernel. Both give the same planes.
+//  * Where the weights are split depends on the kernel: each wave loads the
+//    FP32 weights themselves, 8 consecutive K values of one expert per lane
+//    (the B operand's layout), and splits them in registers
+//    (v_cvt_pk_bf16_f32, two values at a time) -- in the pipelined kernel
+//    for large batches, where the split hides under the MFMAs and the FP32
+//    weights are 2/3 of the bytes of three planes, and in the 128-token-tile
+//    kernel below 4096 tokens; that kernel from 4096 tokens instead reads
+//    planes a kernel of their own writes once per call in MFMA fragment
+//    order (one 16-byte load per fragment). Both give the same planes.
 //  * Block tile up to 128 tokens x 256 experts (all of them at E = 256, so the
 //    input is read from HBM once), four waves of up to 128 x 64. The input
 //    rows, shared by the four waves, go through a ring of LDS stages filled
@@ -48,6 +50,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTargetBlocks = 480;   // about two blocks per CU
 constexpr int kPipeTargetBlocks = 256;   // one block per CU (proj_pipe_kernel)
+#ifndef MOE_PIPE_SPLIT_IN_REGS
+#define MOE_PIPE_SPLIT_IN_REGS 1
+#endif
+constexpr bool kPipeSplitInRegs = MOE_PIPE_SPLIT_IN_REGS;
 
 // ---------------------------------------------------------------- split ----
 
@@ -348,8 +354,11 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
 //
 // Pipeline: every K-step s issues one group of loads for step s + kLook -- one
 // direct-to-LDS 16-byte load of the input stage per wave (the eight waves
-// fill the 8 KB stage of 256 rows x 16 columns) and the wave's three 16-byte
-// weight fragments (one per BF16 plane) into one of kLook + 1 register sets.
+// fill the 8 KB stage of 256 rows x 16 columns) and the wave's weights into
+// one of kLook + 1 register sets: two 16-byte loads of FP32 weights, split
+// into the three BF16 planes at the step that uses them (FP32W; measured
+// 101 -> 98 us at 8192 tokens and no split kernel), or three 16-byte
+// fragments of the split kernel's planes.
 // Loads complete in issue order, so waiting until at most (kLook - 1) groups
 // are outstanding (s_waitcnt vmcnt) means step s's group has landed while
 // the next kLook - 1 stay in flight; a barrier without a memory fence then
@@ -384,9 +393,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // weight planes in its L2 when nsplit divides 8) and token tile b / nsplit;
 // the expert tile is tile / tiles_m. Requires (kend - kbeg) to be a positive
 // multiple of 64 for every slice (plan_route checks it).
+template <bool FP32W>
 __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2))) void proj_pipe_kernel(
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w_frags, int T, int H, int E, int kslice,
-    int nsplit, int tiles_m, float* __restrict__ partials) {
+    const uint16_t* __restrict__ a, const float* __restrict__ W, const uint16_t* __restrict__ w_frags, int T,
+    int H, int E, int kslice, int nsplit, int tiles_m, float* __restrict__ partials) {
+    constexpr int kLoads = FP32W ? 3 : 4;   // loads per wave and step: the input, then the weights
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
@@ -417,6 +428,13 @@ __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2)))
                             (static_cast<size_t>(n_tile) * (H / kKC) + kbeg / kKC) * (3 * G * kWave) +
                             wave * kWave + lane;
     bf16x8_t bq[kPipeSets][3];
+    // FP32W: the wave's FP32 weights themselves, 8 consecutive K values of
+    // expert (lane & 31) per lane (the B operand's layout; experts past E read
+    // expert E - 1, whose results are never stored), split into the three
+    // BF16 planes in registers when used
+    const float* w_src = W + static_cast<size_t>(min(n_tile * kPipeBN + wave * 32 + (lane & 31), E - 1)) * H +
+                         kbeg + 8 * (lane >> 5);
+    float4 wq[kPipeSets][2];
     // The blocks of one XCD run the same K-slice in step: each starts its walk
     // over the slice at an offset of its own (two K-steps per token tile) so
     // that at any moment they read different lines of the shared weight
@@ -427,8 +445,14 @@ __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2)))
     auto issue = [&](int step, int set) {
         const int s = step + rot < nst ? step + rot : step + rot - nst;
         __builtin_amdgcn_global_load_lds(a_src + s * kKC, a_dst + set * kPipeStage, 16, 0, 0);
+        if constexpr (FP32W) {
+            const float4* src = reinterpret_cast<const float4*>(w_src + s * kKC);
+            wq[set][0] = src[0];
+            wq[set][1] = src[1];
+        } else {
 #pragma unroll
-        for (int p = 0; p < 3; ++p) bq[set][p] = b_src[static_cast<size_t>(s) * (3 * G * kWave) + p * G * kWave];
+            for (int p = 0; p < 3; ++p) bq[set][p] = b_src[static_cast<size_t>(s) * (3 * G * kWave) + p * G * kWave];
+        }
     };
 
     if (nst > 0) {
@@ -443,7 +467,7 @@ __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2)))
             for (int ph = 0; ph < kPipeSets; ++ph) {
                 const int s = s0 + ph;
                 __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<(kLook - 1) * kPipeLoads>();   // step s's loads have landed
+                wait_vmcnt<(kLook - 1) * kLoads>();   // step s's loads have landed
                 __builtin_amdgcn_s_barrier();              // ... in every wave
                 __builtin_amdgcn_sched_barrier(0);
                 issue(min(s + kLook, nst - 1), (ph + kLook) % kPipeSets);
@@ -453,11 +477,18 @@ __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
                 for (int mt = 0; mt < kPipeMT; ++mt)
                     av[mt] = *reinterpret_cast<const bf16x8_t*>(base + slot_bytes(mt * 32 + (lane & 31), lane >> 5));
+                bf16x8_t b[3];
+                if constexpr (FP32W) {
+                    split_fragment(wq[ph], b[0], b[1], b[2]);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < 3; ++p) b[p] = bq[ph][p];
+                }
 #pragma unroll
                 for (int p = 0; p < 3; ++p)
 #pragma unroll
                     for (int mt = 0; mt < kPipeMT; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bq[ph][p], acc[mt], 0, 0, 0);
+                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], b[p], acc[mt], 0, 0, 0);
             }
             s0 += kPipeSets;
         } while (s0 < nst);
@@ -528,6 +559,7 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
         const int nsplit = ceil_div(H, kslice);
         if ((tm * tn * nsplit) % kPipeTargetBlocks == 0) {
             p.pipe = true;
+            p.presplit = !kPipeSplitInRegs;
             p.nt = 2;                               // fragment groups of 256-expert tiles
             p.tiles_m = tm;
             p.tiles_n = tn;
@@ -556,9 +588,14 @@ int launch_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uin
 
 int run_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uint16_t* w_frags, int T, int H,
              int E, float* partials, void* stream) {
-    if (p.pipe)
-        return launch(proj_pipe_kernel, dim3(p.tiles_m * p.tiles_n * p.nsplit), dim3(kPipeBlock), kPipeLds, stream,
-                      a, w_frags, T, H, E, p.kslice, p.nsplit, p.tiles_m, partials);
+    if (p.pipe) {
+        const dim3 grid(p.tiles_m * p.tiles_n * p.nsplit);
+        if (!p.presplit)
+            return launch(proj_pipe_kernel<true>, grid, dim3(kPipeBlock), kPipeLds, stream, a, W, w_frags, T, H, E,
+                          p.kslice, p.nsplit, p.tiles_m, partials);
+        return launch(proj_pipe_kernel<false>, grid, dim3(kPipeBlock), kPipeLds, stream, a, W, w_frags, T, H, E,
+                      p.kslice, p.nsplit, p.tiles_m, partials);
+    }
 #define MOE_PROJ(NA, MT, NT) \
     if (p.na == NA && p.mt == MT && p.nt == NT) \
         return launch_proj<NA, MT, NT>(p, a, W, w_frags, T, H, E, partials, stream);
