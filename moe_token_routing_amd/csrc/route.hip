@@ -376,7 +376,6 @@ constexpr int kPipeBN = 32 * kPipeWaves;         // 256 experts
 constexpr int kLook = 3;                         // steps of loads in flight
 constexpr int kPipeSets = kLook + 1;             // register sets = LDS stages
 constexpr int kPipeStage = kPipeBM * 32;         // 8 KB: 256 rows x 16 BF16
-constexpr int kPipeLoads = 4;                    // loads per wave and step
 constexpr size_t kPipeLds = static_cast<size_t>(kPipeSets) * kPipeStage;
 static_assert(kPipeBM * 2 / kWave == kPipeWaves, "one input load per wave and step");
 static_assert(kPipeSets == 4, "the main loop is unrolled over four sets");

@@ -22,6 +22,12 @@
 // rank by (key, id). The sigmoid of the k winners is recomputed from their logits for
 // the weights, summed in pick order in FP32 and divided once.
 // E <= 512: keys in registers. Larger E: keys and logits staged per wave in LDS.
+// For E <= 512 the exact FP64 sigmoid is first avoided: approximate keys from
+// the FP32 hardware exp and reciprocal select a provable superset of the picks
+// (filter_select), and only those few get exact keys and are ranked; the
+// exact selection above runs only when that superset has more than 64
+// members (mass ties). The kernel is bound by VALU issue (a wave64 op holds a
+// 16-lane SIMD for four cycles), which this cuts by about three times.
 #include <cmath>
 
 #include "launch.hpp"
@@ -38,6 +44,12 @@ constexpr int kMaxPicks = MOE_MAX_TOPK;
 // measured at 512 experts, top-22: route 235 -> 211 us; at top-6 and top-8
 // the rounds stay faster by 1-4 us.
 constexpr int kThresholdPicks = 12;
+// Keys first through the FP32 hardware sigmoid (exact FP64 sigmoid only for
+// the few candidates that can be among the picks); see filter_select.
+#ifndef MOE_SELECT_FILTER
+#define MOE_SELECT_FILTER 1
+#endif
+constexpr bool kSelectFilter = MOE_SELECT_FILTER;
 
 // Monotone map of FP32 keys to unsigned integers; -0 counts as +0 and NaN
 // maps to 0, below every number. (A lane with no candidate left is tracked
@@ -67,6 +79,159 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 __device__ __forceinline__ uint32_t round_winner(bool has, uint32_t bk, uint32_t be) {
     const uint32_t kmax = __reduce_max_sync(~0ull, has ? bk : 0u);
     return __reduce_min_sync(~0ull, (has && bk == kmax) ? be : 0xFFFFFFFFu);
+}
+
+// The k-th largest of the wave's live keys (the largest v with at least k
+// live keys >= v), found bit by bit from the top: each step counts with one
+// ballot per register slot, and the count and the bound stay scalar. Every
+// key shares the bits above the highest bit where the smallest and the
+// largest key differ, so the search starts below it.
+// With coarse = true the search stops at the bit whose step, at the keys'
+// magnitude, is 2^-16 or less: the result is then a lower bound of the k-th
+// largest key within 2^-15 of it (what filter_select needs).
+template <int EPL, bool COARSE = false>
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[EPL], uint32_t live, int k) {
+    uint32_t lo_key = 0xFFFFFFFFu, hi_key = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if ((live >> i) & 1u) {
+            lo_key = key[i] < lo_key ? key[i] : lo_key;
+            hi_key = key[i] > hi_key ? key[i] : hi_key;
+        }
+    lo_key = __reduce_min_sync(~0ull, lo_key);
+    hi_key = __reduce_max_sync(~0ull, hi_key);
+    const uint32_t diff = lo_key ^ hi_key;
+    const int top = diff ? 31 - __clz(diff) : -1;   // -1: all keys equal
+    uint32_t thr = top < 0 ? lo_key : (top == 31 ? 0u : (lo_key & ~((2u << top) - 1u)));
+    int last = 0;
+    if constexpr (COARSE) {
+        // one step of bit b spans 2^(b + e - 23) at binary exponent e, so
+        // with e the largest exponent among the keys, bits below 7 - e are
+        // finer than 2^-16 and left at zero (thr only decreases)
+        const uint32_t ehi = ((hi_key & 0x80000000u ? hi_key : ~hi_key) >> 23) & 0xFFu;
+        const uint32_t elo = ((lo_key & 0x80000000u ? lo_key : ~lo_key) >> 23) & 0xFFu;
+        const int e = static_cast<int>(ehi > elo ? ehi : elo) - 127;
+        last = min(31, max(0, 7 - e));
+        if (top < 0) thr = lo_key & ~((1u << last) - 1u);
+    }
+#pragma unroll 1
+    for (int b = top; b >= last; --b) {
+        const uint32_t cand = thr | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(((live >> i) & 1u) && key[i] >= cand));
+        if (cnt >= k) thr = cand;
+    }
+    return thr;
+}
+
+// Inverse of ordered_key for the keys of numbers (not 0, which stands for NaN).
+__device__ __forceinline__ float key_value(uint32_t o) {
+    return __uint_as_float(o & 0x80000000u ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// sigmoid(l) in FP32 hardware approximations, 1 / (1 + 2^(-l log2 e)) with
+// v_exp_f32 and v_rcp_f32: its absolute error is below 2^-17 for every l
+// (the exponent's argument carries a relative error of 2^-24, so 2^x one of
+// |x| ln2 2^-24 < 2^-17.5 while |x| < 128 -- beyond, the sigmoid is within
+// 2^-128 of 0 or 1 and so is this -- and the sigmoid's slope is at most 1/4;
+// exp and rcp add a few ulp). NaN stays NaN, +-inf give 1 and 0.
+__device__ __forceinline__ float sigmoid_approx(float l) {
+    const float e = __builtin_amdgcn_exp2f(-l * 1.44269504088896341f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Per-wave LDS of the filtered selection: the candidates (compacted) and the
+// picks in order.
+struct FilterLds {
+    float cand_l[kSelectWaves][kWave];
+    int32_t cand_id[kSelectWaves][kWave];
+    int32_t pick_id[kSelectWaves][kMaxPicks];
+    float pick_s[kSelectWaves][kMaxPicks];
+};
+
+// Selection of one valid token through approximate keys. A = approx sigmoid +
+// bias differs from the exact key K = RN32(RN32(sigmoid) + bias) by at most
+// d = 2^-17 + 2^-25 + ulp(K). Let A_k be the k-th largest approximate key:
+// the k experts with the largest A have exact keys > A_k - d, so the exact
+// k-th largest key is above A_k - d, and every expert of the exact top k has
+// A > A_k - 2d. The experts with A >= A_k - M (M = 2^-15 + |A_k| 2^-20 > 2d)
+// are therefore a superset of the top k -- typically exactly k of them. They
+// are compacted one per lane, their exact keys computed (FP64 sigmoid rounded
+// once, as everywhere else), and each is ranked among them by (key
+// descending, id ascending): the same picks, order and weights as the exact
+// selection over all experts. Returns false (nothing written) when the k-th
+// approximate key is NaN or more than 64 experts pass; the caller then runs
+// the exact selection. A_k only enters through a lower bound of it within
+// 2^-15 (kth_largest, coarse): any bound below A_k keeps the superset, and
+// one close to it keeps the set small.
+template <int EPL>
+__device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, const float (&lg)[EPL],
+                                              const float* __restrict__ bias, int k, int32_t* __restrict__ ids,
+                                              float* __restrict__ w, FilterLds& sh) {
+    const int wv = threadIdx.x / kWave;
+    float A[EPL];
+    uint32_t oa[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const bool l = (live >> i) & 1u;
+        A[i] = l ? sigmoid_approx(lg[i]) + bias[e0 + i] : 0.f;
+        oa[i] = l ? ordered_key(A[i]) : 0u;
+    }
+    // a lower bound of the k-th largest approximate key, within 2^-15 of it
+    const uint32_t kth = kth_largest<EPL, true>(oa, live, k);
+    if (kth == 0u) return false;   // the k-th approximate key is NaN (or the bound reaches it)
+    const float kf = key_value(kth);
+    const float lo = kf - (0x1p-15f + fabsf(kf) * 0x1p-20f);
+    uint32_t cand = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cand |= static_cast<uint32_t>(((live >> i) & 1u) && A[i] >= lo) << i;
+    const uint64_t below = lanemask_lt();
+    int C = 0, pos = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const uint64_t b = __ballot((cand >> i) & 1u);
+        C += __popcll(b);
+        pos += __popcll(b & below);
+    }
+    if (C > kWave) return false;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if ((cand >> i) & 1u) {
+            sh.cand_l[wv][pos] = lg[i];
+            sh.cand_id[wv][pos] = e0 + i;
+            ++pos;
+        }
+    // (LDS accesses of one wave complete in order; the fences keep the
+    // compiler from moving them across)
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const bool mine = lane < C;
+    const float l = mine ? sh.cand_l[wv][lane] : 0.f;
+    const int id = mine ? sh.cand_id[wv][lane] : 0;
+    const float s = mine ? sigmoid_rn(l) : 0.f;
+    const uint32_t key = mine ? ordered_key(s + bias[id]) : 0u;
+    int rank = 0;
+#pragma unroll 1
+    for (int m = 0; m < C; ++m) {
+        const uint32_t km = __builtin_amdgcn_readlane(key, m);
+        const int im = __builtin_amdgcn_readlane(id, m);
+        rank += (km > key || (km == key && im < id)) ? 1 : 0;
+    }
+    if (mine && rank < k) {
+        sh.pick_id[wv][rank] = id;
+        sh.pick_s[wv][rank] = s;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const float my_s = lane < k ? sh.pick_s[wv][lane] : 0.f;
+    const int my_id = lane < k ? sh.pick_id[wv][lane] : -1;
+    float total = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) total += lane_value(my_s, j);
+    if (lane < k) {
+        ids[lane] = my_id;
+        w[lane] = my_s / total;
+    }
+    return true;
 }
 
 // The k picks' weights: sigmoid of each winner's logit, FP32 sum in pick
@@ -171,16 +336,6 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
             }
         }
     }
-    uint32_t key[EPL];
-    uint32_t live = 0;   // bit i: expert EPL*lane + i still a candidate
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        key[i] = 0u;
-        if (valid && i < n) {
-            key[i] = ordered_key(sigmoid_rn(lg[i]) + bias[e0 + i]);
-            live |= 1u << i;
-        }
-    }
     int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
     float* w = topk_w + static_cast<size_t>(t) * k;
     if (!valid) {
@@ -190,8 +345,18 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
         }
         return;
     }
-    // full lanes of a valid token: every expert of the lane is a candidate
-    if constexpr (FULL) live = (1u << EPL) - 1u;
+    // bit i: expert EPL*lane + i still a candidate (full lanes: all of them)
+    uint32_t live = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) live |= static_cast<uint32_t>(FULL || i < n) << i;
+    if constexpr (kSelectFilter) {
+        __shared__ FilterLds fsh;
+        if (filter_select<EPL>(lane, e0, live, lg, bias, k, ids, w, fsh)) return;
+    }
+    // exact keys of every expert
+    uint32_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) key[i] = ((live >> i) & 1u) ? ordered_key(sigmoid_rn(lg[i]) + bias[e0 + i]) : 0u;
 
     int my_id = -1;
     float my_l = 0.f;
@@ -220,31 +385,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
             }
         }
     } else {
-        // The k-th largest key: the largest v with at least k candidates
-        // whose key is >= v, found bit by bit from the top (each step counts
-        // with one ballot per register slot; the count and the bound stay
-        // scalar). Every key shares the bits above the highest bit where the
-        // smallest and the largest key differ, so the search starts below.
-        uint32_t lo_key = 0xFFFFFFFFu, hi_key = 0u;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if ((live >> i) & 1u) {
-                lo_key = key[i] < lo_key ? key[i] : lo_key;
-                hi_key = key[i] > hi_key ? key[i] : hi_key;
-            }
-        lo_key = __reduce_min_sync(~0ull, lo_key);
-        hi_key = __reduce_max_sync(~0ull, hi_key);
-        const uint32_t diff = lo_key ^ hi_key;
-        const int top = diff ? 31 - __clz(diff) : -1;   // -1: all keys equal
-        uint32_t thr = top < 0 ? lo_key : (top == 31 ? 0u : (lo_key & ~((2u << top) - 1u)));
-#pragma unroll 1
-        for (int b = top; b >= 0; --b) {
-            const uint32_t cand = thr | (1u << b);
-            int cnt = 0;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(((live >> i) & 1u) && key[i] >= cand));
-            if (cnt >= k) thr = cand;
-        }
+        const uint32_t thr = kth_largest<EPL>(key, live, k);
         // The picks: every key above it, then the keys equal to it with the
         // lowest expert ids (ids run lane-major, e = EPL lane + i).
         uint32_t gt = 0u, eq = 0u;

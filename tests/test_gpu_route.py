@@ -262,3 +262,34 @@ def test_route_is_deterministic():
         again = [host(t) for t in m.route(hidden, W, bias, mask, w.k)]
         for a, b in zip(first, again):
             np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (256, 8), (256, 6), (512, 22), (300, 8), (200, 13)])
+def test_route_logits_in_near_threshold_clusters(E, k):
+    """The selection keeps only the experts whose approximate FP32 key is
+    within a small margin of the k-th largest one and computes exact keys for
+    those. Clusters of logits far closer than that margin around the k-th
+    place -- spaced 2^-22 apart, so keys differ in their last bits or tie
+    exactly -- give candidate sets of about k + 20 (ranked exactly) and of more
+    than 64 (the exact selection over all experts); bias steps of one ulp and
+    negative logits too. Bit for bit against the oracle."""
+    require_gpu()
+    g = np.random.default_rng(E * 31 + k)
+    T = 48
+    lg = (g.standard_normal((T, E)) * 0.5 - 3.0).astype(np.float32)   # far below the cluster
+    for t in range(T):
+        size = [k + 20, 70, k, 2 * k, min(E, 100), k + 1][t % 6]
+        size = min(size, E)
+        cols = g.choice(E, size=size, replace=False)
+        base = np.float32(g.uniform(-1.0, 2.0))
+        lg[t, cols] = base + (g.integers(-8, 9, size=size) * 2.0 ** -22).astype(np.float32)
+    lg[5, :] = 0.75                                              # every key equal
+    bias = np.zeros(E, np.float32)
+    bias[::3] = np.float32(2.0 ** -23)                          # one-ulp steps near 1/2 .. 1
+    mask = np.ones(T, np.uint8)
+    mask[9] = 0
+    note("route logits-in near-threshold clusters E=%d k=%d" % (E, k))
+    _, ids, wt = m.route(None, None, dev(bias), dev(mask), k, logits=dev(lg))
+    ids_o, w_o = O.route_from_logits(lg, bias, mask, k)
+    np.testing.assert_array_equal(host(ids), ids_o)
+    np.testing.assert_array_equal(host(wt), w_o)
