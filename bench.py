@@ -12,6 +12,10 @@ E=256, k=8, 5% invalid tokens). Prints one JSON line.
 Schedules (the headline is the default `auto`: the serial schedule launched
 eagerly, the fastest at every batch size measured):
   serial         the four calls in order on one stream
+  prepare        norm + quant forked onto a second stream beside the dispatch
+                 and joined before the combine (so it shares the GPU with
+                 neither the projection nor the combine); the fork and join
+                 cost more than the dispatch time they hide
   overlap        route on the main stream, then norm + quant forked onto a
                  second stream beside dispatch -> combine (it depends on none
                  of them); the step joins back into the main stream, so it
@@ -242,7 +246,7 @@ def main():
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
                     help="skip the 1 GiB device-copy reference bandwidth")
-    ap.add_argument("--schedule", choices=["auto", "overlap", "overlap-route", "serial"], default="auto",
+    ap.add_argument("--schedule", choices=["auto", "prepare", "overlap", "overlap-route", "serial"], default="auto",
                     help="headline schedule: norm+quant on a second stream beside dispatch + combine "
                          "(overlap) or beside the route (overlap-route), or all on one stream (serial); "
                          "auto = serial (the fastest at every batch size measured)")
@@ -349,6 +353,19 @@ def main():
         combine_()
         main.wait_stream(aux)              # join: the step ends when both are done
 
+    def step_prepare():
+        # norm + quant on the second stream beside the dispatch (latency-bound,
+        # a few blocks), joined before the combine, so it never shares the
+        # GPU with the projection or the combine's HBM stream
+        main = torch.cuda.current_stream(dev)
+        route_()
+        aux.wait_stream(main)              # fork
+        with torch.cuda.stream(aux):
+            norm_quant_()
+        dispatch_()
+        main.wait_stream(aux)              # join before the combine
+        combine_()
+
     def step_overlap():
         # the projection is power-bound, so norm + quant goes beside the
         # latency-bound dispatch and the combine rather than beside it
@@ -371,7 +388,8 @@ def main():
 
     if args.schedule == "auto":
         args.schedule = "serial"
-    head_step = {"overlap": step_overlap, "overlap-route": step_overlap_route, "serial": step_serial}[args.schedule]
+    head_step = {"prepare": step_prepare, "overlap": step_overlap, "overlap-route": step_overlap_route,
+                 "serial": step_serial}[args.schedule]
     # one step on a side stream (graph capture wants the work seen once off
     # the capture stream), then the W warm-up steps on the launch stream
     # itself, eager or replayed, so that nothing first-time lands in the
@@ -396,7 +414,8 @@ def main():
 
     # headline: exactly K steps between two synchronizations
     ms_per_step = timed(head_fn, args.steps)
-    head_name = {"overlap": "norm+quant on a second stream beside dispatch + combine",
+    head_name = {"prepare": "norm+quant on a second stream beside the dispatch, joined before the combine",
+                 "overlap": "norm+quant on a second stream beside dispatch + combine",
                  "overlap-route": "norm+quant on a second stream beside the route",
                  "serial": "serial"}[args.schedule] + \
         (", HIP graph replay" if args.graph else ", eager launches")
@@ -412,6 +431,8 @@ def main():
     serial_ms = timed(step_serial, args.steps)
     timed(step_overlap, 5)
     overlap_eager_ms = timed(step_overlap, args.steps)
+    timed(step_prepare, 5)
+    prepare_eager_ms = timed(step_prepare, args.steps)
     timed(step_overlap_route, 5)
     overlap_route_ms = timed(step_overlap_route, args.steps)
 
@@ -535,7 +556,8 @@ def main():
         "expert_fc1": fc1,
         "expert_fc1_swiglu": fc1_swiglu,
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
-                      "serial_eager_ms": round(serial_ms, 4), "overlap_eager_ms": round(overlap_eager_ms, 4),
+                      "serial_eager_ms": round(serial_ms, 4), "prepare_eager_ms": round(prepare_eager_ms, 4),
+                      "overlap_eager_ms": round(overlap_eager_ms, 4),
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),
                       "overlap_graph_ms": round(overlap_graph_ms, 4),
                       "serial_graph_ms": round(serial_graph_ms, 4),
