@@ -1,16 +1,20 @@
 """Benchmark of the MoE routing-and-combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-                    [--schedule overlap|overlap-route|serial] [--graph]
+                    [--schedule fused|serial|prepare|overlap|overlap-route] [--graph]
 
 One step is one pass of the whole path over one batch of synthetic input:
-moe_route -> moe_dispatch -> moe_combine, and moe_norm_quant_nvfp4, with
+moe_route -> moe_dispatch -> moe_combine, and moe_norm_quant_nvfp4 (or
+moe_route_dispatch in place of the first two), with
 inputs resident in HBM and every output and workspace allocated before the
 timed region. The default workload is the 8192-token prefill batch (H=8192,
 E=256, k=8, 5% invalid tokens). Prints one JSON line.
 
-Schedules (the headline is the default `auto`: the serial schedule launched
-eagerly, the fastest at every batch size measured):
+Schedules (the headline is the default `auto`: the fused schedule launched
+eagerly):
+  fused          moe_route_dispatch (route and dispatch in one call, the
+                 selection counting the dispatch's tile histograms), then
+                 norm + quant and the combine, in order on one stream
   serial         the four calls in order on one stream
   prepare        norm + quant forked onto a second stream beside the dispatch
                  and joined before the combine (so it shares the GPU with
@@ -32,7 +36,8 @@ eagerly, the fastest at every batch size measured):
 
 Alongside the throughput the line carries:
   stages        per-call mean duration (HIP events on the launch stream, from
-                a serial eager pass) and algorithmic bytes / achieved GB/s
+                a serial eager pass; route_dispatch from a fused pass) and
+                algorithmic bytes / achieved GB/s
   schedules     ms per step of every schedule, and of the serial one with the
                 256 MB last-level cache flushed before each step (cold); the
                 p10 / median / p90 of single serial steps (HIP events)
@@ -246,7 +251,8 @@ def main():
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
                     help="skip the 1 GiB device-copy reference bandwidth")
-    ap.add_argument("--schedule", choices=["auto", "prepare", "overlap", "overlap-route", "serial"], default="auto",
+    ap.add_argument("--schedule", choices=["auto", "fused", "prepare", "overlap", "overlap-route", "serial"],
+                    default="auto",
                     help="headline schedule: norm+quant on a second stream beside dispatch + combine "
                          "(overlap) or beside the route (overlap-route), or all on one stream (serial); "
                          "auto = serial (the fastest at every batch size measured)")
@@ -310,6 +316,7 @@ def main():
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
     ws_r = torch.empty(max(1, m.route_workspace_bytes(T, H, E, k, hdt)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, m.dispatch_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev)
+    ws_rd = torch.empty(max(1, m.route_dispatch_workspace_bytes(T, H, E, k, hdt)), dtype=torch.uint8, device=dev)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
@@ -326,6 +333,10 @@ def main():
     def dispatch_():
         m.dispatch(ids, E, counts=counts, offsets=offsets, perm=perm, dest=dest, workspace=ws_d)
 
+    def route_dispatch_():
+        m.route_dispatch(hidden, W, bias, mask, k, logits=logits, topk_ids=ids, topk_w=tw, counts=counts,
+                         offsets=offsets, perm=perm, dest=dest, workspace=ws_rd)
+
     def norm_quant_():
         m.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs, packed=packed, scales=scales)
 
@@ -340,6 +351,15 @@ def main():
             call()
         if ev is not None:
             ev[4].record(main)
+
+    def step_fused(ev=None):
+        main = torch.cuda.current_stream(dev)
+        for j, call in enumerate((route_dispatch_, norm_quant_, combine_)):
+            if ev is not None:
+                ev[j].record(main)
+            call()
+        if ev is not None:
+            ev[3].record(main)
 
     aux = torch.cuda.Stream(device=dev)   # default priority
 
@@ -387,9 +407,9 @@ def main():
         return (time.perf_counter() - t0) * 1000.0 / steps
 
     if args.schedule == "auto":
-        args.schedule = "serial"
+        args.schedule = "fused"
     head_step = {"prepare": step_prepare, "overlap": step_overlap, "overlap-route": step_overlap_route,
-                 "serial": step_serial}[args.schedule]
+                 "serial": step_serial, "fused": step_fused}[args.schedule]
     # one step on a side stream (graph capture wants the work seen once off
     # the capture stream), then the W warm-up steps on the launch stream
     # itself, eager or replayed, so that nothing first-time lands in the
@@ -417,7 +437,8 @@ def main():
     head_name = {"prepare": "norm+quant on a second stream beside the dispatch, joined before the combine",
                  "overlap": "norm+quant on a second stream beside dispatch + combine",
                  "overlap-route": "norm+quant on a second stream beside the route",
-                 "serial": "serial"}[args.schedule] + \
+                 "serial": "serial",
+                 "fused": "serial, route and dispatch in one call (moe_route_dispatch)"}[args.schedule] + \
         (", HIP graph replay" if args.graph else ", eager launches")
 
     # serial eager pass with per-call events on the launch stream (stage times)
@@ -429,6 +450,12 @@ def main():
     # every other schedule gets untimed steps of its own first (its streams'
     # first launches stay out of its figure, as the headline's do)
     serial_ms = timed(step_serial, args.steps)
+    # the fused form with per-call events (route + dispatch as one call)
+    fused_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_fused(fused_events[i])
+    torch.cuda.synchronize()
+    fused_ms = timed(step_fused, args.steps)
     timed(step_overlap, 5)
     overlap_eager_ms = timed(step_overlap, args.steps)
     timed(step_prepare, 5)
@@ -451,6 +478,7 @@ def main():
 
     overlap_graph_ms = ms_per_step if args.graph and args.schedule == "overlap" else graph_ms(step_overlap)
     serial_graph_ms = ms_per_step if args.graph and args.schedule == "serial" else graph_ms(step_serial)
+    fused_graph_ms = ms_per_step if args.graph and args.schedule == "fused" else graph_ms(step_fused)
 
     # cold: flush the 256 MB last-level cache (a 512 MiB write) before each step
     cold_ms = None
@@ -510,6 +538,11 @@ def main():
         rank_block["GBps"] = round(nbytes["norm_quant"] / (rank_block["ms"] * 1e-3) / 1e9, 1)
         stages["norm_quant_rank_block"] = rank_block
     stages["route"]["proj_TFLOPs_fp32_equiv"] = round(proj_flop / (stage_ms["route"] * 1e-3) / 1e12, 2)
+    rd_ms = float(np.mean([fused_events[i][0].elapsed_time(fused_events[i][1]) for i in range(args.steps)]))
+    rd_bytes = nbytes["route"] + nbytes["dispatch"]
+    stages["route_dispatch"] = {"ms": round(rd_ms, 4), "bytes": rd_bytes,
+                                "GBps": round(rd_bytes / (rd_ms * 1e-3) / 1e9, 1),
+                                "note": "moe_route_dispatch: the fused call, from the fused pass"}
 
     comb_gbs = nbytes["combine"] / (stage_ms["combine"] * 1e-3) / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
@@ -556,7 +589,9 @@ def main():
         "expert_fc1": fc1,
         "expert_fc1_swiglu": fc1_swiglu,
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
-                      "serial_eager_ms": round(serial_ms, 4), "prepare_eager_ms": round(prepare_eager_ms, 4),
+                      "serial_eager_ms": round(serial_ms, 4), "fused_eager_ms": round(fused_ms, 4),
+                      "fused_graph_ms": round(fused_graph_ms, 4),
+                      "prepare_eager_ms": round(prepare_eager_ms, 4),
                       "overlap_eager_ms": round(overlap_eager_ms, 4),
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),
                       "overlap_graph_ms": round(overlap_graph_ms, 4),

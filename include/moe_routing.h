@@ -11,6 +11,8 @@
  *                         permutation of the routed slots by expert
  *                         (moe_dispatch_noalloc: the same without a workspace,
  *                         for callers that cannot allocate)
+ *   moe_route_dispatch    moe_route followed by moe_dispatch in one call, the
+ *                         selection counting the dispatch's tile histograms
  *   moe_norm_quant_nvfp4  RMSNorm of the expert input with one BF16 rounding,
  *                         fused with NVFP4 quantisation (E2M1 codes, E4M3
  *                         block-16 scales, static global scale); the
@@ -155,6 +157,36 @@ size_t moe_dispatch_workspace_bytes(int T, int k, int E);
 int moe_dispatch(const int32_t* topk_ids, int T, int k, int E,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_dispatch — moe_route, then moe_dispatch of its topk_ids, in one
+ * call.
+ *
+ * Defined by the two calls above: TensorRT-LLM PR #21356, "Router
+ * projection" and "Routing", for the route; lmdeploy PR #4835, MoE gate v2
+ * notes, for the dispatch, whose gate fuses the expert histogram into the
+ * pass that produces the ids. Here the selection adds each valid pick into
+ * the histogram of its tile of slots as it writes it (integer atomics, so
+ * the counts do not depend on arrival order), and the separate histogram
+ * pass of moe_dispatch is skipped. The projection clears those histograms
+ * first (in logits-in mode a small kernel does).
+ *
+ * Arguments: those of moe_route, then the four outputs of moe_dispatch
+ * (counts [E], offsets [E+1], perm [T*k], dest [T*k]); same meaning, layout,
+ * ranges and checks as in the two calls. Every output is bit-identical to
+ * moe_route followed by moe_dispatch on the same inputs.
+ *   workspace   at least moe_route_dispatch_workspace_bytes(T, H, E, k,
+ *               hidden_dtype, logits_in) bytes (may be NULL when that is 0):
+ *               moe_route's workspace, then the tile histograms.
+ * Errors: those of either call.
+ */
+size_t moe_route_dispatch_workspace_bytes(int T, int H, int E, int k, int hidden_dtype, int logits_in);
+
+int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                       const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+                       float* logits, int32_t* topk_ids, float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_dispatch_noalloc — moe_dispatch without a workspace argument, for

@@ -38,6 +38,9 @@ _SIGNATURES = {
     "moe_dispatch_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_dispatch": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_dispatch_noalloc": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_dispatch_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "moe_route_dispatch": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_float, _c_int, _c_int, _c_int, _c_int,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_norm_quant_nvfp4": (_c_int, [_vp, _vp, _c_float, _c_float, _vp, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_norm_quant_nvfp4_rank_block": (_c_int, [_vp, _c_int, _vp, _c_float, _c_float, _vp, _c_int, _c_int,
                                                  _vp, _vp, _vp]),
@@ -113,12 +116,9 @@ def route_workspace_bytes(T: int, H: int, E: int, k: int, hidden_dtype: int, log
     return int(lib().moe_route_workspace_bytes(T, H, E, k, hidden_dtype, int(bool(logits_in))))
 
 
-def route(hidden: Optional[torch.Tensor], W: Optional[torch.Tensor], bias: torch.Tensor,
-          token_mask: torch.Tensor, k: int, scale: float = 1.0, *, logits: Optional[torch.Tensor] = None,
-          topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-          workspace: Optional[torch.Tensor] = None):
-    """moe_route. hidden: [T,H] bf16 or fp32 (None: logits-in mode, `logits`
-    [T,E] fp32 is then an input). Returns (logits, topk_ids int32, topk_w fp32)."""
+def _route_io(hidden, W, bias, token_mask, k, logits, topk_ids, topk_w):
+    """Checks and allocates moe_route's arguments; returns (T, H, E, dtype,
+    logits, topk_ids, topk_w)."""
     dev = bias.device
     E = bias.shape[0]
     _need(bias, "bias", (torch.float32,), (E,))
@@ -146,10 +146,39 @@ def route(hidden: Optional[torch.Tensor], W: Optional[torch.Tensor], bias: torch
         topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _need(topk_ids, "topk_ids", (torch.int32,), (T, k), dev)
     _need(topk_w, "topk_w", (torch.float32,), (T, k), dev)
-    ws_bytes = route_workspace_bytes(T, H, E, k, dtype, hidden is None)
+    return T, H, E, dtype, logits, topk_ids, topk_w
+
+
+def _dispatch_io(dev, T, k, E, counts, offsets, perm, dest):
+    """Checks and allocates moe_dispatch's outputs."""
+    n = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm = torch.empty(n, dtype=torch.int32, device=dev) if perm is None else perm
+    dest = torch.empty(n, dtype=torch.int32, device=dev) if dest is None else dest
+    _need(counts, "counts", (torch.int32,), (E,), dev)
+    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    _need(perm, "perm", (torch.int32,), (n,), dev)
+    _need(dest, "dest", (torch.int32,), (n,), dev)
+    return counts, offsets, perm, dest
+
+
+def _workspace(workspace, ws_bytes, dev):
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, ws_len
+
+
+def route(hidden: Optional[torch.Tensor], W: Optional[torch.Tensor], bias: torch.Tensor,
+          token_mask: torch.Tensor, k: int, scale: float = 1.0, *, logits: Optional[torch.Tensor] = None,
+          topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None):
+    """moe_route. hidden: [T,H] bf16 or fp32 (None: logits-in mode, `logits`
+    [T,E] fp32 is then an input). Returns (logits, topk_ids int32, topk_w fp32)."""
+    dev = bias.device
+    T, H, E, dtype, logits, topk_ids, topk_w = _route_io(hidden, W, bias, token_mask, k, logits, topk_ids, topk_w)
+    workspace, ws_len = _workspace(workspace, route_workspace_bytes(T, H, E, k, dtype, hidden is None), dev)
     _check("moe_route", lib().moe_route(
         _ptr(hidden), dtype, _ptr(W), _ptr(bias), _ptr(token_mask), float(scale), T, H, E, k,
         _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), ws_len, _stream(dev)))
@@ -168,19 +197,8 @@ def dispatch(topk_ids: torch.Tensor, E: int, *, counts=None, offsets=None, perm=
     if topk_ids.dim() != 2:
         raise ValueError("topk_ids must be [T,k]")
     T, k = topk_ids.shape
-    n = T * k
-    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
-    perm = torch.empty(n, dtype=torch.int32, device=dev) if perm is None else perm
-    dest = torch.empty(n, dtype=torch.int32, device=dev) if dest is None else dest
-    _need(counts, "counts", (torch.int32,), (E,), dev)
-    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
-    _need(perm, "perm", (torch.int32,), (n,), dev)
-    _need(dest, "dest", (torch.int32,), (n,), dev)
-    ws_bytes = dispatch_workspace_bytes(T, k, E)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    counts, offsets, perm, dest = _dispatch_io(dev, T, k, E, counts, offsets, perm, dest)
+    workspace, ws_len = _workspace(workspace, dispatch_workspace_bytes(T, k, E), dev)
     _check("moe_dispatch", lib().moe_dispatch(
         _ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(dest),
         _ptr(workspace), ws_len, _stream(dev)))
@@ -196,18 +214,33 @@ def dispatch_noalloc(topk_ids: torch.Tensor, E: int, *, counts=None, offsets=Non
     if topk_ids.dim() != 2:
         raise ValueError("topk_ids must be [T,k]")
     T, k = topk_ids.shape
-    n = T * k
-    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
-    perm = torch.empty(n, dtype=torch.int32, device=dev) if perm is None else perm
-    dest = torch.empty(n, dtype=torch.int32, device=dev) if dest is None else dest
-    _need(counts, "counts", (torch.int32,), (E,), dev)
-    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
-    _need(perm, "perm", (torch.int32,), (n,), dev)
-    _need(dest, "dest", (torch.int32,), (n,), dev)
+    counts, offsets, perm, dest = _dispatch_io(dev, T, k, E, counts, offsets, perm, dest)
     _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
         _ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(dest), _stream(dev)))
     return counts, offsets, perm, dest
+
+
+def route_dispatch_workspace_bytes(T: int, H: int, E: int, k: int, hidden_dtype: int,
+                                   logits_in: bool = False) -> int:
+    return int(lib().moe_route_dispatch_workspace_bytes(T, H, E, k, hidden_dtype, int(bool(logits_in))))
+
+
+def route_dispatch(hidden: Optional[torch.Tensor], W: Optional[torch.Tensor], bias: torch.Tensor,
+                   token_mask: torch.Tensor, k: int, scale: float = 1.0, *, logits=None, topk_ids=None,
+                   topk_w=None, counts=None, offsets=None, perm=None, dest=None,
+                   workspace: Optional[torch.Tensor] = None):
+    """moe_route_dispatch: route() then dispatch() of its ids in one call.
+    Returns (logits, topk_ids, topk_w, counts, offsets, perm, dest)."""
+    dev = bias.device
+    T, H, E, dtype, logits, topk_ids, topk_w = _route_io(hidden, W, bias, token_mask, k, logits, topk_ids, topk_w)
+    counts, offsets, perm, dest = _dispatch_io(dev, T, k, E, counts, offsets, perm, dest)
+    workspace, ws_len = _workspace(workspace, route_dispatch_workspace_bytes(T, H, E, k, dtype, hidden is None),
+                                   dev)
+    _check("moe_route_dispatch", lib().moe_route_dispatch(
+        _ptr(hidden), dtype, _ptr(W), _ptr(bias), _ptr(token_mask), float(scale), T, H, E, k,
+        _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(dest),
+        _ptr(workspace), ws_len, _stream(dev)))
+    return logits, topk_ids, topk_w, counts, offsets, perm, dest
 
 
 def norm_quant_nvfp4(x: torch.Tensor, norm_w: torch.Tensor, gain_center: float, eps: float,

@@ -39,6 +39,7 @@
 //    applies the scale and picks the top k.
 #include <cmath>
 
+#include "dispatch.hpp"
 #include "launch.hpp"
 #include "select.hpp"
 
@@ -54,6 +55,15 @@ constexpr int kPipeTargetBlocks = 256;   // one block per CU (proj_pipe_kernel)
 #define MOE_PIPE_SPLIT_IN_REGS 1
 #endif
 constexpr bool kPipeSplitInRegs = MOE_PIPE_SPLIT_IN_REGS;
+
+// Zeroes p[0, n) over the whole grid: the per-tile expert histograms that
+// the fused route + dispatch's selection counts into (run by the projection,
+// which precedes the selection on the stream, after its own stores).
+__device__ __forceinline__ void clear_range(int32_t* __restrict__ p, long long n) {
+    for (long long i = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<long long>(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
 
 // ---------------------------------------------------------------- split ----
 
@@ -215,7 +225,8 @@ __device__ __forceinline__ void split_fragment(const float4 (&w)[2], bf16x8_t& b
 template <int NA, int MT, int NT, bool PRESPLIT>
 __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2))) void proj_kernel(
     const uint16_t* __restrict__ a_planes, const float* __restrict__ W, const uint16_t* __restrict__ w_frags,
-    int T, int H, int E, int kslice, int nsplit, int tiles_m, float* __restrict__ partials) {
+    int T, int H, int E, int kslice, int nsplit, int tiles_m, float* __restrict__ partials,
+    int32_t* __restrict__ clear, long long clear_n) {
     using S = GemmShape<NA, MT, NT>;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int tid = threadIdx.x;
@@ -338,6 +349,7 @@ __global__ __launch_bounds__(kGemmBlock) __attribute__((amdgpu_waves_per_eu(2)))
                 if (row < T && col < E) out[static_cast<size_t>(row) * E + col] = acc[mt][nt][i];
             }
         }
+    clear_range(clear, clear_n);
 }
 
 // ------------------------------------------------------ pipelined gemm ----
@@ -395,7 +407,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <bool FP32W>
 __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2))) void proj_pipe_kernel(
     const uint16_t* __restrict__ a, const float* __restrict__ W, const uint16_t* __restrict__ w_frags, int T,
-    int H, int E, int kslice, int nsplit, int tiles_m, float* __restrict__ partials) {
+    int H, int E, int kslice, int nsplit, int tiles_m, float* __restrict__ partials,
+    int32_t* __restrict__ clear, long long clear_n) {
     constexpr int kLoads = FP32W ? 3 : 4;   // loads per wave and step: the input, then the weights
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int lane = __lane_id();
@@ -507,6 +520,7 @@ __global__ __launch_bounds__(kPipeBlock) __attribute__((amdgpu_waves_per_eu(2)))
                 if (row < T) out[static_cast<size_t>(row) * E + col] = acc[mt][i];
             }
     }
+    clear_range(clear, clear_n);
 }
 
 // From this many tokens the weights are split once per call into
@@ -575,51 +589,41 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
 
 template <int NA, int MT, int NT>
 int launch_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uint16_t* w_frags, int T, int H,
-                int E, float* partials, void* stream) {
+                int E, float* partials, int32_t* clear, long long clear_n, void* stream) {
     using S = GemmShape<NA, MT, NT>;
     const dim3 grid(p.tiles_m * p.tiles_n * p.nsplit);
     if (p.presplit)
         return launch(proj_kernel<NA, MT, NT, true>, grid, dim3(kGemmBlock), S::LDS, stream, a, W, w_frags, T, H,
-                      E, p.kslice, p.nsplit, p.tiles_m, partials);
+                      E, p.kslice, p.nsplit, p.tiles_m, partials, clear, clear_n);
     return launch(proj_kernel<NA, MT, NT, false>, grid, dim3(kGemmBlock), S::LDS, stream, a, W, w_frags, T, H, E,
-                  p.kslice, p.nsplit, p.tiles_m, partials);
+                  p.kslice, p.nsplit, p.tiles_m, partials, clear, clear_n);
 }
 
+// The projection's launch; it also zeroes clear[0, clear_n) (nothing when
+// clear_n is 0).
 int run_proj(const RoutePlan& p, const uint16_t* a, const float* W, const uint16_t* w_frags, int T, int H,
-             int E, float* partials, void* stream) {
+             int E, float* partials, int32_t* clear, long long clear_n, void* stream) {
     if (p.pipe) {
         const dim3 grid(p.tiles_m * p.tiles_n * p.nsplit);
         if (!p.presplit)
             return launch(proj_pipe_kernel<true>, grid, dim3(kPipeBlock), kPipeLds, stream, a, W, w_frags, T, H, E,
-                          p.kslice, p.nsplit, p.tiles_m, partials);
+                          p.kslice, p.nsplit, p.tiles_m, partials, clear, clear_n);
         return launch(proj_pipe_kernel<false>, grid, dim3(kPipeBlock), kPipeLds, stream, a, W, w_frags, T, H, E,
-                      p.kslice, p.nsplit, p.tiles_m, partials);
+                      p.kslice, p.nsplit, p.tiles_m, partials, clear, clear_n);
     }
 #define MOE_PROJ(NA, MT, NT) \
     if (p.na == NA && p.mt == MT && p.nt == NT) \
-        return launch_proj<NA, MT, NT>(p, a, W, w_frags, T, H, E, partials, stream);
+        return launch_proj<NA, MT, NT>(p, a, W, w_frags, T, H, E, partials, clear, clear_n, stream);
     MOE_PROJ(1, 1, 1) MOE_PROJ(1, 1, 2) MOE_PROJ(1, 2, 1) MOE_PROJ(1, 2, 2) MOE_PROJ(1, 4, 1) MOE_PROJ(1, 4, 2)
     MOE_PROJ(3, 1, 1) MOE_PROJ(3, 1, 2) MOE_PROJ(3, 2, 1) MOE_PROJ(3, 2, 2)
 #undef MOE_PROJ
     return MOE_ERR_BAD_SHAPE;
 }
 
-}  // namespace
-}  // namespace moe
-
-extern "C" size_t moe_route_workspace_bytes(int T, int H, int E, int k, int hidden_dtype, int logits_in) {
-    using namespace moe;
-    if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || logits_in) return 0;
-    if (hidden_dtype != MOE_DTYPE_F32 && hidden_dtype != MOE_DTYPE_BF16) return 0;
-    const RoutePlan p = plan_route(T, H, E, hidden_dtype);
-    return p.w_planes_bytes + p.a_planes_bytes + p.partial_bytes;
-}
-
-extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, const float* bias,
-                         const uint8_t* token_mask, float scale, int T, int H, int E, int k,
-                         float* logits, int32_t* topk_ids, float* topk_w, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-    using namespace moe;
+// Argument checks of moe_route (before any launch); a moe_status.
+int check_route(const void* hidden, int hidden_dtype, const float* W, const float* bias, const uint8_t* token_mask,
+                float scale, int T, int H, int E, int k, const float* logits, const int32_t* topk_ids,
+                const float* topk_w) {
     const bool logits_in = hidden == nullptr;
     if (!logits_in && hidden_dtype != MOE_DTYPE_F32 && hidden_dtype != MOE_DTYPE_BF16)
         return MOE_ERR_BAD_DTYPE;
@@ -633,12 +637,24 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
     if (!bias || !token_mask || !logits || !topk_ids || !topk_w) return MOE_ERR_NULL_ARG;
     if (!logits_in && !W) return MOE_ERR_NULL_ARG;
     if (!all_aligned16(hidden, W, bias, token_mask, logits, topk_ids, topk_w)) return MOE_ERR_ALIGN;
-    if (logits_in)
-        return run_select(nullptr, 0, 1.f, 1, bias, token_mask, T, E, k, logits, topk_ids, topk_w, stream);
+    return MOE_OK;
+}
 
-    const size_t need = moe_route_workspace_bytes(T, H, E, k, hidden_dtype, 0);
-    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+// The route's launches for T > 0 on checked arguments and a large enough
+// workspace. With hist set (hist_n int32 of per-tile expert histograms of
+// hist_tile slots each), the histograms are zeroed and the selection counts
+// every valid pick into them.
+int run_route(const void* hidden, int hidden_dtype, const float* W, const float* bias, const uint8_t* token_mask,
+              float scale, int T, int H, int E, int k, float* logits, int32_t* topk_ids, float* topk_w,
+              void* workspace, int32_t* hist, long long hist_n, int hist_tile, void* stream) {
+    if (hidden == nullptr) {   // logits in: the selection only
+        if (hist) {
+            const int rc = run_clear(hist, hist_n, stream);
+            if (rc) return rc;
+        }
+        return run_select(nullptr, 0, 1.f, 1, bias, token_mask, T, E, k, logits, topk_ids, topk_w, hist,
+                          hist_tile, stream);
+    }
     const RoutePlan p = plan_route(T, H, E, hidden_dtype);
     char* ws = static_cast<char*>(workspace);
     uint16_t* w_planes = reinterpret_cast<uint16_t*>(ws);
@@ -663,8 +679,83 @@ extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, c
         if (rc) return rc;
         a = a_planes;
     }
-    const int rc = run_proj(p, a, W, w_planes, T, H, E, partials, stream);
+    const int rc = run_proj(p, a, W, w_planes, T, H, E, partials, hist, hist ? hist_n : 0, stream);
     if (rc) return rc;
-    return run_select(partials, p.nsplit, scale, 0, bias, token_mask, T, E, k, logits, topk_ids,
-                      topk_w, stream);
+    return run_select(partials, p.nsplit, scale, 0, bias, token_mask, T, E, k, logits, topk_ids, topk_w, hist,
+                      hist_tile, stream);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" size_t moe_route_workspace_bytes(int T, int H, int E, int k, int hidden_dtype, int logits_in) {
+    using namespace moe;
+    if (T <= 0 || H <= 0 || E <= 0 || k <= 0 || logits_in) return 0;
+    if (hidden_dtype != MOE_DTYPE_F32 && hidden_dtype != MOE_DTYPE_BF16) return 0;
+    const RoutePlan p = plan_route(T, H, E, hidden_dtype);
+    return p.w_planes_bytes + p.a_planes_bytes + p.partial_bytes;
+}
+
+extern "C" int moe_route(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                         const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+                         float* logits, int32_t* topk_ids, float* topk_w, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    const int rc = check_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids,
+                               topk_w);
+    if (rc || T == 0) return rc;
+    if (hidden) {
+        const size_t need = moe_route_workspace_bytes(T, H, E, k, hidden_dtype, 0);
+        if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+    }
+    return run_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
+                     workspace, nullptr, 0, 1, stream);
+}
+
+namespace {
+
+// Bytes of the fused call's per-tile histograms (none with one tile).
+size_t fused_hist_bytes(int T, int k, int E) {
+    const long long n = static_cast<long long>(T) * k;
+    if (n <= 0) return 0;
+    const moe::DispatchTiles d = moe::dispatch_tiles(n);
+    if (d.tiles <= 1) return 0;
+    return (static_cast<size_t>(d.tiles) * E * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" size_t moe_route_dispatch_workspace_bytes(int T, int H, int E, int k, int hidden_dtype,
+                                                     int logits_in) {
+    using namespace moe;
+    if (T <= 0 || H <= 0 || E <= 0 || E > MOE_MAX_EXPERTS || k <= 0 || k > MOE_MAX_TOPK) return 0;
+    if (!logits_in && hidden_dtype != MOE_DTYPE_F32 && hidden_dtype != MOE_DTYPE_BF16) return 0;
+    return round256(moe_route_workspace_bytes(T, H, E, k, hidden_dtype, logits_in)) + fused_hist_bytes(T, k, E);
+}
+
+extern "C" int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                                  const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+                                  float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, int32_t* dest, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    int rc = check_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w);
+    if (rc) return rc;
+    rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
+    if (rc) return rc;
+    if (T == 0) return run_dispatch_empty(counts, offsets, E, stream);
+    const size_t route_bytes = round256(moe_route_workspace_bytes(T, H, E, k, hidden_dtype, hidden == nullptr));
+    const size_t hist_bytes = fused_hist_bytes(T, k, E);
+    if (route_bytes + hist_bytes > 0) {
+        if (!workspace || workspace_bytes < route_bytes + hist_bytes) return MOE_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+    }
+    const long long n = static_cast<long long>(T) * k;
+    const DispatchTiles d = dispatch_tiles(n);
+    int32_t* hist = hist_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + route_bytes) : nullptr;
+    rc = run_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
+                   workspace, hist, static_cast<long long>(d.tiles) * E, d.tile, stream);
+    if (rc) return rc;
+    return run_place(topk_ids, n, E, counts, offsets, perm, dest, hist, stream);
 }

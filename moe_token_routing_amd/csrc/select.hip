@@ -162,13 +162,13 @@ struct FilterLds {
 // descending, id ascending): the same picks, order and weights as the exact
 // selection over all experts. Returns false (nothing written) when the k-th
 // approximate key is NaN or more than 64 experts pass; the caller then runs
-// the exact selection. A_k only enters through a lower bound of it within
+// the exact selection. Lane j < k returns pick j's id in `pick`. A_k only enters through a lower bound of it within
 // 2^-15 (kth_largest, coarse): any bound below A_k keeps the superset, and
 // one close to it keeps the set small.
 template <int EPL>
 __device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, const float (&lg)[EPL],
                                               const float* __restrict__ bias, int k, int32_t* __restrict__ ids,
-                                              float* __restrict__ w, FilterLds& sh) {
+                                              float* __restrict__ w, FilterLds& sh, int& pick) {
     const int wv = threadIdx.x / kWave;
     float A[EPL];
     uint32_t oa[EPL];
@@ -231,6 +231,7 @@ __device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, c
         ids[lane] = my_id;
         w[lane] = my_s / total;
     }
+    pick = my_id;
     return true;
 }
 
@@ -245,6 +246,19 @@ __device__ __forceinline__ void write_picks(int lane, int k, int my_id, float my
     if (lane < k) {
         ids[lane] = my_id;
         w[lane] = my_s / total;
+    }
+}
+
+// With `hist` set, lane j < k counts token t's pick j into the expert
+// histogram of its tile of dispatch slots: hist[(t k + j) / hist_tile][id]
+// += 1 (slot t k + j is pick j of token t, as moe_dispatch numbers them).
+// Integer additions commute, so the counts do not depend on the order in
+// which waves arrive; the add returns nothing, so the wave does not wait.
+__device__ __forceinline__ void count_pick(int32_t* __restrict__ hist, int hist_tile, int E, int t, int k,
+                                          int lane, int id) {
+    if (hist && lane < k && id >= 0) {
+        const long long slot = static_cast<long long>(t) * k + lane;
+        __hip_atomic_fetch_add(hist + (slot / hist_tile) * E + id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -290,7 +304,8 @@ template <int EPL, int BATCH, bool THRESHOLD, bool FULL>
 __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
-    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    int32_t* __restrict__ hist, int hist_tile) {
     const int lane = __lane_id();
     const int t = blockIdx.x * kSelectWaves + threadIdx.x / kWave;
     if (t >= T) return;   // whole wave leaves together
@@ -351,7 +366,11 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     for (int i = 0; i < EPL; ++i) live |= static_cast<uint32_t>(FULL || i < n) << i;
     if constexpr (kSelectFilter) {
         __shared__ FilterLds fsh;
-        if (filter_select<EPL>(lane, e0, live, lg, bias, k, ids, w, fsh)) return;
+        int pick = -1;
+        if (filter_select<EPL>(lane, e0, live, lg, bias, k, ids, w, fsh, pick)) {
+            count_pick(hist, hist_tile, E, t, k, lane, pick);
+            return;
+        }
     }
     // exact keys of every expert
     uint32_t key[EPL];
@@ -451,6 +470,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
         my_l = lane < k ? pick_l[wv][lane] : 0.f;
     }
     write_picks(lane, k, my_id, my_l, ids, w);
+    count_pick(hist, hist_tile, E, t, k, lane, my_id);
 }
 
 // Any E: each wave stages its token's keys in its own LDS region (dynamic
@@ -462,7 +482,8 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
 __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
-    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+    float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    int32_t* __restrict__ hist, int hist_tile) {
     extern __shared__ uint32_t sel_lds[];
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
@@ -551,16 +572,17 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     __threadfence_block();
     const float my_l = lane < k ? logits[static_cast<size_t>(t) * E + my_id] : 0.f;
     write_picks(lane, k, my_id, my_l, ids, w);
+    count_pick(hist, hist_tile, E, t, k, lane, my_id);
 }
 
 template <int EPL, int BATCH>
 int launch_select_reg2(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
                        const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
-                       void* stream) {
+                       int32_t* hist, int hist_tile, void* stream) {
     const dim3 grid(ceil_div(T, kSelectWaves));
 #define MOE_SELECT(THR, FULL)                                                                                 \
     return launch(select_reg_kernel<EPL, BATCH, THR, FULL>, grid, dim3(kSelectBlock), 0, stream, partials, nsplit, \
-                  scale, logits_in, bias, mask, T, E, k, logits, ids, w)
+                  scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile)
     const bool full = E == EPL * kWave;   // then E % 4 == 0 and every row is 16-byte aligned
     if (k >= kThresholdPicks) {
         if (full) MOE_SELECT(true, true);
@@ -574,27 +596,27 @@ int launch_select_reg2(const float* partials, int nsplit, float scale, int logit
 template <int EPL>
 int launch_select_reg(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
                       const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
-                      void* stream) {
+                      int32_t* hist, int hist_tile, void* stream) {
     if (nsplit > 2 * kSplitBatch)
         return launch_select_reg2<EPL, 4 * kSplitBatch>(partials, nsplit, scale, logits_in, bias, mask, T, E, k,
-                                                        logits, ids, w, stream);
+                                                        logits, ids, w, hist, hist_tile, stream);
     return launch_select_reg2<EPL, kSplitBatch>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits,
-                                                ids, w, stream);
+                                                ids, w, hist, hist_tile, stream);
 }
 
 }  // namespace
 
 int run_select(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
                const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
-               void* stream) {
+               int32_t* hist, int hist_tile, void* stream) {
     const int epl = ceil_div(E, kWave);
-    if (epl <= 1) return launch_select_reg<1>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
-    if (epl <= 2) return launch_select_reg<2>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
-    if (epl <= 4) return launch_select_reg<4>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
-    if (epl <= 8) return launch_select_reg<8>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, stream);
+    if (epl <= 1) return launch_select_reg<1>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile, stream);
+    if (epl <= 2) return launch_select_reg<2>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile, stream);
+    if (epl <= 4) return launch_select_reg<4>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile, stream);
+    if (epl <= 8) return launch_select_reg<8>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile, stream);
     const size_t lds = static_cast<size_t>(kSelectWaves) * E * sizeof(uint32_t);
     return launch(select_lds_kernel, dim3(ceil_div(T, kSelectWaves)), dim3(kSelectBlock), lds, stream,
-                  partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w);
+                  partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile);
 }
 
 }  // namespace moe

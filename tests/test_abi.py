@@ -29,6 +29,7 @@ def test_every_declared_function_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"moe_status_string", "moe_route_workspace_bytes", "moe_route",
                           "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_dispatch_noalloc",
+                          "moe_route_dispatch_workspace_bytes", "moe_route_dispatch",
                           "moe_norm_quant_nvfp4",
                           "moe_norm_quant_nvfp4_rank_block", "moe_combine",
                           "moe_expert_fc1_workspace_bytes", "moe_expert_fc1_nvfp4",
@@ -114,6 +115,34 @@ def test_route_rejects_before_launch(lib):
     assert call(ws=None) == -4 and call(wsb=16) == -4
     assert call(T=0) == 0
     assert call(ids=V((1 << 20) + 8)) == -7
+
+
+def test_route_dispatch_rejects_before_launch(lib):
+    f = lib.moe_route_dispatch
+
+    def call(hidden=FAKE, dtype=1, W=FAKE, bias=FAKE, mask=FAKE, scale=1.0, T=4, H=64, E=16, k=4,
+             logits=FAKE, ids=FAKE, w=FAKE, counts=FAKE, offsets=FAKE, perm=FAKE, dest=FAKE, ws=FAKE,
+             wsb=1 << 30):
+        return f(hidden, dtype, W, bias, mask, scale, T, H, E, k, logits, ids, w, counts, offsets, perm, dest,
+                 ws, wsb, None)
+
+    # the route's checks
+    assert call(dtype=7) == -3
+    assert call(k=17) == -2 and call(k=0) == -2 and call(E=4097, k=4) == -2 and call(H=24) == -2
+    assert call(T=-2) == -2 and call(scale=float("inf")) == -5
+    assert call(bias=None) == -1 and call(W=None) == -1 and call(ids=V((1 << 20) + 8)) == -7
+    # the dispatch's
+    assert call(counts=None) == -1 and call(perm=None) == -1 and call(dest=V((1 << 20) + 4)) == -7
+    # the workspace: the route's part and the tile histograms
+    assert call(ws=None) == -4 and call(wsb=16) == -4
+    need = m.route_dispatch_workspace_bytes(4096, 64, 16, 4, m.MOE_DTYPE_BF16)
+    assert call(T=4096, wsb=need - 1) == -4
+    assert need == m.route_workspace_bytes(4096, 64, 16, 4, m.MOE_DTYPE_BF16) + m.dispatch_workspace_bytes(4096, 4, 16)
+    assert need % 256 == 0
+    # logits-in needs only the tile histograms, and one tile of slots none
+    assert m.route_dispatch_workspace_bytes(200, 16, 16, 4, m.MOE_DTYPE_BF16, logits_in=True) == 0
+    assert m.route_dispatch_workspace_bytes(2000, 16, 16, 4, m.MOE_DTYPE_BF16, logits_in=True) == \
+        m.dispatch_workspace_bytes(2000, 4, 16) > 0
 
 
 def test_dispatch_rejects_before_launch(lib):

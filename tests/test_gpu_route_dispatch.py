@@ -1,0 +1,177 @@
+"""moe_route_dispatch (the route and the dispatch in one call, the selection
+counting the dispatch's tile histograms) against the two separate calls and
+the oracle.
+
+Every output -- logits, ids, weights, counts, offsets, perm, dest -- must be
+bit-identical to moe_route followed by moe_dispatch on the same inputs, and
+the dispatch outputs must equal the oracle's dispatch of the ids (lmdeploy PR
+#4835, MoE gate v2: the gate counts its expert histogram as it routes). The
+cases cover each form the place step takes: one tile of slots (no
+histograms), histograms summed in the place step, and a separate scan (tile
+count squared times E beyond the fused limit); BF16 and FP32 input (the two
+projection kernels), logits-in mode (histograms cleared by a kernel of their
+own), top-22 picks straddling tiles, invalid tokens, zero tokens, repeated
+calls, and replays of a captured graph with changed inputs, whose
+histograms must be cleared again on every replay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as wl
+from gpu_helpers import DEV, dev, host, note, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+m = pytest.importorskip("moe_token_routing_amd")
+
+NAMES = ("logits", "topk_ids", "topk_w", "counts", "offsets", "perm", "dest")
+
+
+def _separate(hidden_d, W_d, bias_d, mask_d, k, scale=1.0, logits_d=None):
+    if hidden_d is None:
+        lg, ids, w = m.route(None, None, bias_d, mask_d, k, logits=logits_d)
+    else:
+        lg, ids, w = m.route(hidden_d, W_d, bias_d, mask_d, k, scale)
+    counts, offsets, perm, dest = m.dispatch(ids, bias_d.shape[0])
+    return [host(t) for t in (lg, ids, w, counts, offsets, perm, dest)]
+
+
+def _fused(hidden_d, W_d, bias_d, mask_d, k, scale=1.0, logits_d=None):
+    out = m.route_dispatch(hidden_d, W_d, bias_d, mask_d, k, scale, logits=logits_d)
+    return [host(t) for t in out]
+
+
+def _compare(hidden, W, bias, mask, k, what, scale=1.0, logits=None):
+    require_gpu()
+    T = mask.shape[0]
+    E = bias.shape[0]
+    note("route_dispatch %s T=%d E=%d k=%d" % (what, T, E, k))
+    h_d = None if hidden is None else dev(hidden)
+    W_d = None if W is None else dev(W)
+    b_d, m_d = dev(bias), dev(mask)
+    sep = _separate(h_d, W_d, b_d, m_d, k, scale, None if logits is None else dev(logits))
+    fus = _fused(h_d, W_d, b_d, m_d, k, scale, None if logits is None else dev(logits))
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, fus, sep):
+        np.testing.assert_array_equal(a, b, err_msg="%s: %s differs from route + dispatch" % (what, name))
+    ref = O.dispatch(fus[1], E)
+    for name, g, r in zip(NAMES[3:], fus[3:], ref):
+        np.testing.assert_array_equal(g, r, err_msg="%s: %s differs from the oracle" % (what, name))
+    return fus
+
+
+# (workload, tokens, hidden dtype): tiny and decode are one tile of slots;
+# prefill at 2048 tokens sums 16 tile histograms in the place step, at 8192
+# tokens (the full batch, pipelined projection) 64; large E at 4096 tokens
+# has 32 tiles of 2560 experts, past the fused limit, so the scan runs; wide
+# top-22 at 2000 tokens puts tokens across tile edges.
+@pytest.mark.parametrize("name,T,fp32", [("tiny", None, False), ("decode", None, False),
+                                         ("prefill", 2048, False), ("prefill", None, False),
+                                         ("prefill", 600, True), ("large_e", None, False),
+                                         ("wide_k", 2000, False), ("wide_k", 2000, True)])
+def test_route_dispatch_matches_separate_calls(name, T, fp32):
+    w = wl.WORKLOADS[name]
+    T = w.T if T is None else T
+    hidden = wl.hidden(w, T)
+    if fp32:
+        hidden = (hidden.astype(np.uint32) << 16).view(np.float32)
+    mask = wl.token_mask(w, T)
+    fus = _compare(hidden, wl.router_weight(w), wl.bias(w), mask, w.k, "%s T=%d fp32=%s" % (name, T, fp32))
+    assert fus[3].sum() == int((mask != 0).sum()) * w.k
+
+
+@pytest.mark.parametrize("T,E,k", [(100, 64, 4), (5000, 256, 8), (3000, 512, 22), (40000, 64, 6)])
+def test_route_dispatch_logits_in(T, E, k):
+    g = np.random.default_rng(T + E + k)
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    logits[:, 5] = logits[:, 3]                         # exact ties
+    bias = (g.standard_normal(E) * 0.01).astype(np.float32)
+    mask = (g.uniform(size=T) > 0.15).astype(np.uint8)
+    _compare(None, None, bias, mask, k, "logits-in", logits=logits)
+
+
+def test_route_dispatch_all_invalid_and_zero_tokens():
+    require_gpu()
+    w = wl.WORKLOADS["prefill"]
+    T = 3000
+    mask = np.zeros(T, np.uint8)
+    fus = _compare(wl.hidden(w, T), wl.router_weight(w), wl.bias(w), mask, w.k, "all invalid")
+    assert (fus[3] == 0).all() and (fus[5] == -1).all() and (fus[6] == -1).all()
+    out = m.route_dispatch(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
+                           torch.zeros((16, 64), dtype=torch.float32, device=DEV),
+                           torch.zeros(16, dtype=torch.float32, device=DEV),
+                           torch.zeros(0, dtype=torch.uint8, device=DEV), 4)
+    torch.cuda.synchronize()
+    assert (host(out[3]) == 0).all() and (host(out[4]) == 0).all() and out[5].numel() == 0
+
+
+def test_route_dispatch_repeated_calls_reuse_workspace():
+    """The tile histograms live in the caller's workspace; each call clears
+    them, so calls on one workspace with different inputs stay exact."""
+    require_gpu()
+    w = wl.WORKLOADS["prefill"]
+    T = 4096
+    W_d, b_d = dev(wl.router_weight(w)), dev(wl.bias(w))
+    ws = torch.empty(m.route_dispatch_workspace_bytes(T, w.H, w.E, w.k, m.MOE_DTYPE_BF16), dtype=torch.uint8,
+                     device=DEV)
+    gt = torch.Generator(device=DEV).manual_seed(5)
+    for rep in range(3):
+        note("route_dispatch repeat %d" % rep)
+        h_d = torch.randn((T, w.H), generator=gt, device=DEV).to(torch.bfloat16)
+        m_d = (torch.rand(T, generator=gt, device=DEV) > 0.1 * rep).to(torch.uint8)
+        fus = [host(t) for t in m.route_dispatch(h_d, W_d, b_d, m_d, w.k, workspace=ws)]
+        sep = _separate(h_d, W_d, b_d, m_d, w.k)
+        for name, a, b in zip(NAMES, fus, sep):
+            np.testing.assert_array_equal(a, b, err_msg="repeat %d: %s" % (rep, name))
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_route_dispatch_graph_replay(name):
+    """Captured once, replayed with new inputs copied in place: every replay
+    equals the separate eager calls and the oracle's dispatch."""
+    require_gpu()
+    w = wl.WORKLOADS[name]
+    T = w.T
+    h_d = dev(wl.hidden(w, T))
+    W_d, b_d, m_d = dev(wl.router_weight(w)), dev(wl.bias(w)), dev(wl.token_mask(w, T))
+    outs = dict(logits=torch.empty((T, w.E), dtype=torch.float32, device=DEV),
+                topk_ids=torch.empty((T, w.k), dtype=torch.int32, device=DEV),
+                topk_w=torch.empty((T, w.k), dtype=torch.float32, device=DEV),
+                counts=torch.empty(w.E, dtype=torch.int32, device=DEV),
+                offsets=torch.empty(w.E + 1, dtype=torch.int32, device=DEV),
+                perm=torch.empty(T * w.k, dtype=torch.int32, device=DEV),
+                dest=torch.empty(T * w.k, dtype=torch.int32, device=DEV))
+    ws = torch.empty(max(256, m.route_dispatch_workspace_bytes(T, w.H, w.E, w.k, m.MOE_DTYPE_BF16)),
+                     dtype=torch.uint8, device=DEV)
+
+    def call():
+        m.route_dispatch(h_d, W_d, b_d, m_d, w.k, workspace=ws, **outs)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        note("route_dispatch graph replay %s %d" % (name, rep))
+        gt = torch.Generator(device=DEV).manual_seed(40 + rep)
+        h_d.copy_(torch.randn((T, w.H), generator=gt, device=DEV).to(torch.bfloat16))
+        m_d.copy_((torch.rand(T, generator=gt, device=DEV) > 0.2).to(torch.uint8))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = [host(outs[n]).copy() for n in NAMES]
+        sep = _separate(h_d, W_d, b_d, m_d, w.k)
+        torch.cuda.synchronize()
+        for n, a, b in zip(NAMES, replayed, sep):
+            np.testing.assert_array_equal(a, b, err_msg="replay %d: %s" % (rep, n))
+        ref = O.dispatch(replayed[1], w.E)
+        for n, g, r in zip(NAMES[3:], replayed[3:], ref):
+            np.testing.assert_array_equal(g, r, err_msg="replay %d: %s vs oracle" % (rep, n))
