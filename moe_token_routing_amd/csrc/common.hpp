@@ -63,9 +63,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---- wave reductions (wave64) ---------------------------------------------
 
+// Sum over the wave as a butterfly: v += v[lane ^ d] for d = 32, 16, 8, 4, 2,
+// 1. Partners add the same two values, so every lane ends with the same sum
+// and the order of additions is fixed. The exchanges use no LDS addresses:
+// d = 32 and 16 swap row halves between two copies of v (v_permlane32_swap,
+// v_permlane16_swap: each copy then holds one operand of every lane's
+// addition), d = 8 rotates a 16-lane row by 8 and d = 2, 1 permute quads
+// (DPP), and d = 4 is a ds_swizzle with xor mask 4.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    uint32_t u = __float_as_uint(v);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    u = __float_as_uint(v);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));   // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));   // lane ^ 4 (32-lane groups)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));    // quad [2,3,0,1]
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));    // quad [1,0,3,2]
     return v;
 }
 

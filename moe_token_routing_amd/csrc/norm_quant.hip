@@ -18,7 +18,13 @@
 // lane owns whole 16-element blocks (two neighbouring vectors), so a block's
 // maximum, E4M3 scale (hardware FP8 conversion, clamped to saturate) and
 // reciprocal are computed once, and its 16 codes (hardware FP4 conversion)
-// leave as one 8-byte store, its scale as one byte.
+// leave as one 8-byte store, its scale as one byte. The reciprocal of a
+// block's scale takes at most 256 values per call (one per E4M3 byte), so
+// each block of threads computes them once into an LDS table. For tokens
+// whose sum of squares and rinv are finite, with finite gains (the usual
+// case), the block maximum comes from the unrounded products (one v_max3_f32
+// per pair) and each value is rounded to BF16 in FP32 layout by one
+// conversion; other tokens take the general path. Both give the same bytes.
 //
 // When a block visits several tokens and a token fills whole waves or the
 // whole block, the next token's row is copied into LDS by global_load_lds
@@ -41,54 +47,115 @@ __device__ __forceinline__ float round_to_bf16(float f) {
     return __uint_as_float(f32_to_bf16_rne(f) << 16);
 }
 
+// RN to BF16 of an FP32 value, returned as the FP32 value it represents
+// (one v_cvt_pk_bf16_f32 with a zero low half; v must not be NaN).
+__device__ __forceinline__ float bf16_round(float v) { return __uint_as_float(cvt_pk_bf16(0.f, v)); }
+
 // One 16-element block: normalise (x * gain) * rinv, round once to BF16,
 // take the block maximum, its E4M3 scale byte and the 16 E2M1 codes (element
 // 2j in the low nibble of byte j). Returns the codes, the scale byte in *sf.
+// outs_of[sf] is the block's 1 / (E4M3 value of sf * RN(1 / gs)) (0 when that
+// value is 0), precomputed with the same IEEE operations for every byte.
+// FINITE: the caller has shown that no normalised value can be NaN (finite
+// input and gains, finite rinv), so the block maximum is taken over the
+// unrounded |v| (v_max3_f32) and rounded once: RN to BF16 is monotone and
+// symmetric, so RN(max |v|) = max |RN(v)|, the same value as the general
+// path's maximum over the rounded BF16 magnitudes (which also orders NaN).
+template <bool FINITE>
 __device__ __forceinline__ uint2 encode_block(const uint32_t (&xw)[8], const float (&gain)[16], float rinv,
-                                              float gs, float rcp_gs, uint32_t* sf_out) {
+                                              float gs, const float* outs_of, uint32_t* sf_out) {
     constexpr float kRcp6 = 1.0f / 6.0f;
-    // normalised pairs, rounded once to BF16 (packed)
-    uint32_t yp[8];
+    float y[16];   // the normalised values rounded to BF16, as FP32
+    uint32_t mbits;
+    if constexpr (FINITE) {
+        float vmax = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-        yp[q] = cvt_pk_bf16((bf16_lo(xw[q]) * gain[2 * q]) * rinv, (bf16_hi(xw[q]) * gain[2 * q + 1]) * rinv);
-    // block maximum of |y|: the magnitude bits of non-negative BF16
-    // values order like integers, and a NaN magnitude exceeds inf.
-    uint32_t m = packed_max_u16(yp[0] & 0x7FFF7FFFu, yp[1] & 0x7FFF7FFFu);
+        for (int q = 0; q < 8; ++q) {
+            const float v0 = (bf16_lo(xw[q]) * gain[2 * q]) * rinv;
+            const float v1 = (bf16_hi(xw[q]) * gain[2 * q + 1]) * rinv;
+            vmax = fmaxf(fmaxf(vmax, fabsf(v0)), fabsf(v1));   // v_max3_f32 with |.| modifiers
+            y[2 * q] = bf16_round(v0);
+            y[2 * q + 1] = bf16_round(v1);
+        }
+        mbits = cvt_pk_bf16(0.f, vmax) >> 16;
+    } else {
+        // normalised pairs, rounded once to BF16 (packed)
+        uint32_t yp[8];
 #pragma unroll
-    for (int q = 2; q < 8; ++q) m = packed_max_u16(m, yp[q] & 0x7FFF7FFFu);
-    const uint32_t mbits = max(m & 0xFFFFu, m >> 16);
+        for (int q = 0; q < 8; ++q)
+            yp[q] = cvt_pk_bf16((bf16_lo(xw[q]) * gain[2 * q]) * rinv, (bf16_hi(xw[q]) * gain[2 * q + 1]) * rinv);
+        // block maximum of |y|: the magnitude bits of non-negative BF16
+        // values order like integers, and a NaN magnitude exceeds inf.
+        uint32_t m = packed_max_u16(yp[0] & 0x7FFF7FFFu, yp[1] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int q = 2; q < 8; ++q) m = packed_max_u16(m, yp[q] & 0x7FFF7FFFu);
+        mbits = max(m & 0xFFFFu, m >> 16);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            y[2 * q] = bf16_lo(yp[q]);
+            y[2 * q + 1] = bf16_hi(yp[q]);
+        }
+    }
     const float bmax = __uint_as_float(mbits << 16);
     const float tq = bmax * kRcp6;
     const float s = gs * tq;
     const uint32_t sf = e4m3_scale_code(s);
-    const float sf_f = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sf), 0);
-    const float d = sf_f * rcp_gs;
-    const float outs = (sf_f != 0.f) ? 1.0f / d : 0.f;
+    const float outs = outs_of[sf];
     uint32_t w0 = 0, w1 = 0;
     if (mbits < 0x7F80u && fabsf(outs) < INFINITY) {
         // q = y * out with -0 turned into +0 (fma with a +0 addend, one
         // rounding); the hardware E2M1 conversion with unit scale rounds
         // finite values to nearest even and saturates.
-        w0 = fp4_pair<0>(w0, yp[0], outs);
-        w0 = fp4_pair<1>(w0, yp[1], outs);
-        w0 = fp4_pair<2>(w0, yp[2], outs);
-        w0 = fp4_pair<3>(w0, yp[3], outs);
-        w1 = fp4_pair<0>(w1, yp[4], outs);
-        w1 = fp4_pair<1>(w1, yp[5], outs);
-        w1 = fp4_pair<2>(w1, yp[6], outs);
-        w1 = fp4_pair<3>(w1, yp[7], outs);
+        w0 = fp4_pair<0>(w0, y[0], y[1], outs);
+        w0 = fp4_pair<1>(w0, y[2], y[3], outs);
+        w0 = fp4_pair<2>(w0, y[4], y[5], outs);
+        w0 = fp4_pair<3>(w0, y[6], y[7], outs);
+        w1 = fp4_pair<0>(w1, y[8], y[9], outs);
+        w1 = fp4_pair<1>(w1, y[10], y[11], outs);
+        w1 = fp4_pair<2>(w1, y[12], y[13], outs);
+        w1 = fp4_pair<3>(w1, y[14], y[15], outs);
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            w0 |= e2m1_code(bf16_lo(yp[q]) * outs) << (8 * q);
-            w0 |= e2m1_code(bf16_hi(yp[q]) * outs) << (8 * q + 4);
-            w1 |= e2m1_code(bf16_lo(yp[q + 4]) * outs) << (8 * q);
-            w1 |= e2m1_code(bf16_hi(yp[q + 4]) * outs) << (8 * q + 4);
+            w0 |= e2m1_code(y[2 * q] * outs) << (8 * q);
+            w0 |= e2m1_code(y[2 * q + 1] * outs) << (8 * q + 4);
+            w1 |= e2m1_code(y[8 + 2 * q] * outs) << (8 * q);
+            w1 |= e2m1_code(y[8 + 2 * q + 1] * outs) << (8 * q + 4);
         }
     }
     *sf_out = sf;
     return make_uint2(w0, w1);
+}
+
+// outs_of[c] for every E4M3 byte c (one entry per thread of a 256-thread
+// block, then a barrier): 1 / (value(c) * rcp_gs), IEEE division, 0 when the
+// value is 0; NaN for the NaN codes.
+__device__ __forceinline__ void fill_outs_table(float* outs_of, float rcp_gs) {
+    static_assert(kRowBlock == 256, "one table entry per thread");
+    const int c = threadIdx.x;
+    const float sf_f = __builtin_amdgcn_cvt_f32_fp8(c, 0);
+    const float d = sf_f * rcp_gs;
+    outs_of[c] = (sf_f != 0.f) ? 1.0f / d : 0.f;
+    __syncthreads();
+}
+
+// Whether every gain is finite (then finite input and a finite rinv give
+// no NaN among the normalised values).
+template <int BPT>
+__device__ __forceinline__ bool gains_finite(const float (&gain)[BPT][16]) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ok = ok && fabsf(gain[i][e]) <= 3.40282347e38f;
+    return ok;
+}
+
+// 1 / sqrt(ss / H + eps), IEEE operations; ss / H as a product with 1 / H
+// when H is a power of two (both are the correctly rounded quotient).
+__device__ __forceinline__ float rms_inverse(float ss, int H, float hf, float inv_h, float eps) {
+    const float mean = (H & (H - 1)) == 0 ? ss * inv_h : ss / hf;
+    return 1.0f / sqrtf(mean + eps);
 }
 
 // gains of one 16-element block: centre + weight, in FP32
@@ -118,6 +185,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
     uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     __shared__ float red[kRowBlock / kWave];
+    __shared__ float outs_of[256];
     const int nblk = H >> 4;
     constexpr bool WHOLE = TPT != 0;
     if (WHOLE) tpt = TPT;
@@ -127,8 +195,10 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
                           : static_cast<int>(threadIdx.x) / tpt;
     const int tid = static_cast<int>(threadIdx.x) - sub * tpt;
     const float hf = static_cast<float>(H);
+    const float inv_h = 1.0f / hf;
     const float gs = *global_scale;
     const float rcp_gs = 1.0f / gs;
+    fill_outs_table(outs_of, rcp_gs);
     // gains of this thread's blocks, and where block b of token t starts:
     // src[i] + t * shard8 (16-byte units; both vectors of a block lie in one
     // rank block since shard % 16 == 0)
@@ -144,6 +214,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
         for (int e = 0; e < 16; ++e) gain[i][e] = 0.f;
         if (WHOLE || b < nblk) load_gains(norm_w, b, gain_center, gain[i]);
     }
+    const bool gok = gains_finite<BPT>(gain);
 
     for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
         const int t = t0 + sub;
@@ -166,12 +237,14 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
 #pragma unroll
             for (int q = 0; q < 8; ++q) ss[0] = dot2_sq(xw[i][q], ss[0]);
         token_sum(ss, tpt, red);
-        const float rinv = 1.0f / sqrtf(ss[0] / hf + eps);
+        const float rinv = rms_inverse(ss[0], H, hf, inv_h, eps);
+        const bool finite = gok && ss[0] <= 3.40282347e38f && rinv <= 3.40282347e38f;
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             const int b = tid + i * tpt;
             uint32_t sf;
-            const uint2 codes = encode_block(xw[i], gain[i], rinv, gs, rcp_gs, &sf);
+            const uint2 codes = finite ? encode_block<true>(xw[i], gain[i], rinv, gs, outs_of, &sf)
+                                       : encode_block<false>(xw[i], gain[i], rinv, gs, outs_of, &sf);
             if (WHOLE ? tok_ok : (tok_ok && b < nblk)) {
                 packed[static_cast<size_t>(t) * nblk + b] = codes;
                 scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf);
@@ -214,6 +287,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
     uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     static_assert(TPT == kWave || TPT == kRowBlock, "whole waves or the whole block per token");
     __shared__ float red[2][kRowBlock / kWave];
+    __shared__ float outs_of[256];
     __shared__ u32x4 stage[2 * BPT][kRowBlock];
     constexpr int nblk = BPT * TPT;
     constexpr int tokens_per_block = kRowBlock / TPT;
@@ -222,8 +296,10 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
     const int wave = static_cast<int>(threadIdx.x) / kWave;
     const int wbase = wave * kWave;
     const float hf = static_cast<float>(H);
+    const float inv_h = 1.0f / hf;
     const float gs = *global_scale;
     const float rcp_gs = 1.0f / gs;
+    fill_outs_table(outs_of, rcp_gs);
     float gain[BPT][16];
     size_t src[BPT];
 #pragma unroll
@@ -234,6 +310,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
         src[i] = static_cast<size_t>(rb) * T * shard8 + (v - rb * shard8);
         load_gains(norm_w, b, gain_center, gain[i]);
     }
+    const bool gok = gains_finite<BPT>(gain);
     const int step = gridDim.x * tokens_per_block;
     int t = blockIdx.x * tokens_per_block + sub;
     if (t < T) {
@@ -285,12 +362,14 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
             for (int w = 1; w < kRowBlock / kWave; ++w) ss += red[par][w];
         }
         if (!tok_ok) continue;
-        const float rinv = 1.0f / sqrtf(ss / hf + eps);
+        const float rinv = rms_inverse(ss, H, hf, inv_h, eps);
+        const bool finite = gok && ss <= 3.40282347e38f && rinv <= 3.40282347e38f;
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             const int b = tid + i * TPT;
             uint32_t sf;
-            const uint2 codes = encode_block(xw[i], gain[i], rinv, gs, rcp_gs, &sf);
+            const uint2 codes = finite ? encode_block<true>(xw[i], gain[i], rinv, gs, outs_of, &sf)
+                                       : encode_block<false>(xw[i], gain[i], rinv, gs, outs_of, &sf);
             packed[static_cast<size_t>(t) * nblk + b] = codes;
             scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf);
         }

@@ -31,16 +31,21 @@ __device__ __forceinline__ uint32_t e2m1_code(float q) {
     return c | (q < 0.f ? 8u : 0u);
 }
 
-// Codes of a packed BF16 pair y times `outs` into byte BYTE of `word`:
+// Codes of a pair y0, y1 (or a packed BF16 pair) times `outs` into byte BYTE
+// of `word`:
 // q = y * outs with -0 turned into +0 (an FMA with a +0 addend rounds once,
 // like the product), then v_cvt_scalef32_pk_fp4_f32 with unit scale, which
 // rounds finite values to the nearest E2M1 value (ties to even code),
 // saturates, and puts the first value in the low nibble.
 template <int BYTE>
-__device__ __forceinline__ uint32_t fp4_pair(uint32_t word, uint32_t ypair, float outs) {
-    const float q0 = __builtin_fmaf(bf16_lo(ypair), outs, 0.0f);
-    const float q1 = __builtin_fmaf(bf16_hi(ypair), outs, 0.0f);
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t word, float y0, float y1, float outs) {
+    const float q0 = __builtin_fmaf(y0, outs, 0.0f);
+    const float q1 = __builtin_fmaf(y1, outs, 0.0f);
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q0, q1, 1.0f, BYTE);
+}
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t word, uint32_t ypair, float outs) {
+    return fp4_pair<BYTE>(word, bf16_lo(ypair), bf16_hi(ypair), outs);
 }
 
 // E4M3 byte of a block scale s >= 0 (or NaN): v_cvt_pk_fp8_f32 rounds to the
