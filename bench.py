@@ -253,13 +253,17 @@ def main():
                     help="skip the 1 GiB device-copy reference bandwidth")
     ap.add_argument("--schedule", choices=["auto", "fused", "prepare", "overlap", "overlap-route", "serial"],
                     default="auto",
-                    help="headline schedule: norm+quant on a second stream beside dispatch + combine "
-                         "(overlap) or beside the route (overlap-route), or all on one stream (serial); "
-                         "auto = serial (the fastest at every batch size measured)")
+                    help="headline schedule: route and dispatch in one call then norm+quant and combine "
+                         "(fused), the four calls on one stream (serial), norm+quant on a second stream "
+                         "beside the dispatch (prepare), beside dispatch + combine (overlap) or beside the "
+                         "route (overlap-route); auto = fused")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline schedule from a HIP graph instead of launching it eagerly")
     ap.add_argument("--no-fc1", dest="fc1", action="store_false",
                     help="skip timing the expert FC1 (K 1024, N 2688, 512 experts, top-22)")
+    ap.add_argument("--stage", choices=["route", "dispatch", "route_dispatch", "norm_quant", "combine"],
+                    help="time one call of the path alone, repeated (after one fused step), then exit; "
+                         "with --copy-calib also run a 1 GiB copy (for counter runs)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="serial steps timed after flushing the last-level cache (0: skip)")
     args = ap.parse_args()
@@ -406,6 +410,24 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1000.0 / steps
 
+    if args.stage:
+        # one call of the path, repeated (for counter runs): a fused step
+        # first, so the dispatch and the combine see this batch's routing
+        step_fused()
+        call = {"route": route_, "dispatch": dispatch_, "route_dispatch": route_dispatch_,
+                "norm_quant": norm_quant_, "combine": combine_}[args.stage]
+        for _ in range(args.warmup):
+            call()
+        st = timed(call, args.steps)
+        if args.copy_calib:
+            ca = torch.zeros(1 << 29, dtype=torch.int16, device=dev)
+            cb = torch.empty_like(ca)
+            torch.neg(ca, out=cb)
+            torch.cuda.synchronize()
+            del ca, cb
+        print(json.dumps({"stage": args.stage, "workload": w.name, "ms": round(st, 4), "steps": args.steps,
+                          "copy_calib_GiB": 1 if args.copy_calib else 0}))
+        return
     if args.schedule == "auto":
         args.schedule = "fused"
     head_step = {"prepare": step_prepare, "overlap": step_overlap, "overlap-route": step_overlap_route,
