@@ -21,13 +21,16 @@
 // lowest-id keys equal to it are the picks, and each pick's place is its
 // rank by (key, id). The sigmoid of the k winners is recomputed from their logits for
 // the weights, summed in pick order in FP32 and divided once.
-// E <= 512: keys in registers. Larger E: keys and logits staged per wave in LDS.
-// For E <= 512 the exact FP64 sigmoid is first avoided: approximate keys from
-// the FP32 hardware exp and reciprocal select a provable superset of the picks
-// (filter_select), and only those few get exact keys and are ranked; the
-// exact selection above runs only when that superset has more than 64
-// members (mass ties). The kernel is bound by VALU issue (a wave64 op holds a
-// 16-lane SIMD for four cycles), which this cuts by about three times.
+// E <= 512: keys in registers. Larger E: logits staged per wave in LDS.
+// The exact FP64 sigmoid is first avoided: approximate keys from the FP32
+// hardware exp and reciprocal select a provable superset of the picks
+// (filter_select; the k-th largest of the lanes' maxima bounds the cut), and
+// only those few get exact keys and are ranked; the exact selection above
+// runs only when that superset has more than 64 members (mass ties) or the
+// keys are not finite. The kernel is bound by VALU issue (a wave64 op holds a
+// 16-lane SIMD for four cycles), which this cuts by about three times. Every
+// global load of a token (split partials, biases) is issued before its
+// first store, so no wait for loads also waits for stores.
 #include <cmath>
 
 #include "launch.hpp"
@@ -51,6 +54,7 @@ constexpr int kThresholdPicks = 12;
 #endif
 constexpr bool kSelectFilter = MOE_SELECT_FILTER;
 
+
 // Monotone map of FP32 keys to unsigned integers; -0 counts as +0 and NaN
 // maps to 0, below every number. (A lane with no candidate left is tracked
 // by its own flag, not by a key value.)
@@ -67,7 +71,7 @@ __device__ __forceinline__ float sigmoid_rn(float l) {
 }
 
 constexpr int kSplitBatch = 8;   // split partials loaded before they are added
-constexpr int kLdsBatch = 8;     // a lane's experts loaded (or scanned) at once by select_lds_kernel
+constexpr int kLdsBatch = 8;   // a lane's experts loaded (or scanned) at once by select_lds_kernel
 
 // value of lane `src` (wave-uniform) of v: v_readlane_b32, no LDS round trip
 __device__ __forceinline__ float lane_value(float v, int src) {
@@ -145,63 +149,20 @@ __device__ __forceinline__ float sigmoid_approx(float l) {
 // picks in order.
 struct FilterLds {
     float cand_l[kSelectWaves][kWave];
+    float cand_b[kSelectWaves][kWave];   // the candidate's bias (no gather after the logit stores)
     int32_t cand_id[kSelectWaves][kWave];
     int32_t pick_id[kSelectWaves][kMaxPicks];
     float pick_s[kSelectWaves][kMaxPicks];
 };
 
-// Selection of one valid token through approximate keys. A = approx sigmoid +
-// bias differs from the exact key K = RN32(RN32(sigmoid) + bias) by at most
-// d = 2^-17 + 2^-25 + ulp(K). Let A_k be the k-th largest approximate key:
-// the k experts with the largest A have exact keys > A_k - d, so the exact
-// k-th largest key is above A_k - d, and every expert of the exact top k has
-// A > A_k - 2d. The experts with A >= A_k - M (M = 2^-15 + |A_k| 2^-20 > 2d)
-// are therefore a superset of the top k -- typically exactly k of them. They
-// are compacted one per lane, their exact keys computed (FP64 sigmoid rounded
-// once, as everywhere else), and each is ranked among them by (key
-// descending, id ascending): the same picks, order and weights as the exact
-// selection over all experts. Returns false (nothing written) when the k-th
-// approximate key is NaN or more than 64 experts pass; the caller then runs
-// the exact selection. Lane j < k returns pick j's id in `pick`. A_k only enters through a lower bound of it within
-// 2^-15 (kth_largest, coarse): any bound below A_k keeps the superset, and
-// one close to it keeps the set small.
-template <int EPL>
-__device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, const float (&lg)[EPL],
-                                              const float* __restrict__ bias, int k, int32_t* __restrict__ ids,
-                                              float* __restrict__ w, FilterLds& sh, int& pick) {
+// The C <= 64 candidates in sh.cand_l / cand_b / cand_id (logit, bias and id;
+// this wave's rows, in any order): exact keys (FP64 sigmoid rounded once, plus the bias in FP32), each
+// ranked among them by (key descending, id ascending); the first k are the
+// picks, written with their renormalised weights (sigmoid, FP32 sum in pick
+// order, one division). Returns pick `lane`'s id to lane < k.
+__device__ __forceinline__ int rank_candidates(int lane, int C, int k, int32_t* __restrict__ ids,
+                                               float* __restrict__ w, FilterLds& sh) {
     const int wv = threadIdx.x / kWave;
-    float A[EPL];
-    uint32_t oa[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const bool l = (live >> i) & 1u;
-        A[i] = l ? sigmoid_approx(lg[i]) + bias[e0 + i] : 0.f;
-        oa[i] = l ? ordered_key(A[i]) : 0u;
-    }
-    // a lower bound of the k-th largest approximate key, within 2^-15 of it
-    const uint32_t kth = kth_largest<EPL, true>(oa, live, k);
-    if (kth == 0u) return false;   // the k-th approximate key is NaN (or the bound reaches it)
-    const float kf = key_value(kth);
-    const float lo = kf - (0x1p-15f + fabsf(kf) * 0x1p-20f);
-    uint32_t cand = 0u;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) cand |= static_cast<uint32_t>(((live >> i) & 1u) && A[i] >= lo) << i;
-    const uint64_t below = lanemask_lt();
-    int C = 0, pos = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const uint64_t b = __ballot((cand >> i) & 1u);
-        C += __popcll(b);
-        pos += __popcll(b & below);
-    }
-    if (C > kWave) return false;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        if ((cand >> i) & 1u) {
-            sh.cand_l[wv][pos] = lg[i];
-            sh.cand_id[wv][pos] = e0 + i;
-            ++pos;
-        }
     // (LDS accesses of one wave complete in order; the fences keep the
     // compiler from moving them across)
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -209,7 +170,7 @@ __device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, c
     const float l = mine ? sh.cand_l[wv][lane] : 0.f;
     const int id = mine ? sh.cand_id[wv][lane] : 0;
     const float s = mine ? sigmoid_rn(l) : 0.f;
-    const uint32_t key = mine ? ordered_key(s + bias[id]) : 0u;
+    const uint32_t key = mine ? ordered_key(s + sh.cand_b[wv][lane]) : 0u;
     int rank = 0;
 #pragma unroll 1
     for (int m = 0; m < C; ++m) {
@@ -231,9 +192,81 @@ __device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, c
         ids[lane] = my_id;
         w[lane] = my_s / total;
     }
-    pick = my_id;
+    return my_id;
+}
+
+// Selection of one valid token through approximate keys. A = approx sigmoid +
+// bias differs from the exact key K = RN32(RN32(sigmoid) + bias) by at most
+// d = 2^-17 + 2^-25 + ulp(K). Let A_k be the k-th largest approximate key:
+// the k experts with the largest A have exact keys > A_k - d, so the exact
+// k-th largest key is above A_k - d, and every expert of the exact top k has
+// A > A_k - 2d. For any lower bound t <= A_k, the experts with A >= t - M
+// (M = 2^-15 + max|A| 2^-20 > 2d) are therefore a superset of the top k --
+// typically a few more than k. They are compacted one per lane, their exact
+// keys computed (FP64 sigmoid rounded once, as everywhere else), and each is
+// ranked among them by (key descending, id ascending): the same picks, order
+// and weights as the exact selection over all experts. Returns false
+// (nothing written) when the bound is NaN or infinite, or fewer than k or
+// more than 64 experts pass; the caller then runs the exact selection. Lane
+// j < k returns pick j's id in `pick`.
+template <int EPL>
+__device__ __forceinline__ bool filter_select(int lane, int e0, uint32_t live, const float (&lg)[EPL],
+                                              const float (&bs)[EPL], int k, int32_t* __restrict__ ids,
+                                              float* __restrict__ w, FilterLds& sh, int& pick) {
+    const int wv = threadIdx.x / kWave;
+    float A[EPL];
+    uint32_t oa[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const bool l = (live >> i) & 1u;
+        A[i] = l ? sigmoid_approx(lg[i]) + bs[i] : 0.f;
+        oa[i] = l ? ordered_key(A[i]) : 0u;
+    }
+    // The k-th largest of the lanes' largest approximate keys: k distinct
+    // experts lie at or above it, so it is at most A_k (and a coarse lower
+    // bound of it serves as well); one key per lane to search instead of all
+    // of them (measured: selection at 512 experts, top-22, 32768 tokens 65 ->
+    // 49 us). M's relative term is taken at the largest |A| of the row, which
+    // covers the ulp of every key however far below A_k the bound lies.
+    uint32_t lmax = 0u;
+    float labs = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if ((live >> i) & 1u) {
+            lmax = max(lmax, oa[i]);
+            labs = fmaxf(labs, fabsf(A[i]));
+        }
+    const uint32_t top1[1] = {lmax};
+    const uint32_t kth = kth_largest<1, true>(top1, live != 0u ? 1u : 0u, k);
+    if (kth == 0u) return false;   // fewer than k lanes hold a number
+    // (non-negative values order like their bit patterns)
+    const float amax = __uint_as_float(__reduce_max_sync(~0ull, __float_as_uint(labs)));
+    const float lo = key_value(kth) - (0x1p-15f + amax * 0x1p-20f);
+    uint32_t cand = 0u;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cand |= static_cast<uint32_t>(((live >> i) & 1u) && A[i] >= lo) << i;
+    const uint64_t below = lanemask_lt();
+    int C = 0, pos = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const uint64_t b = __ballot((cand >> i) & 1u);
+        C += __popcll(b);
+        pos += __popcll(b & below);
+    }
+    // (fewer than k: the cut is NaN, an infinite key; then the exact path)
+    if (C < k || C > kWave) return false;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if ((cand >> i) & 1u) {
+            sh.cand_l[wv][pos] = lg[i];
+            sh.cand_b[wv][pos] = bs[i];
+            sh.cand_id[wv][pos] = e0 + i;
+            ++pos;
+        }
+    pick = rank_candidates(lane, C, k, ids, w, sh);
     return true;
 }
+
 
 // The k picks' weights: sigmoid of each winner's logit, FP32 sum in pick
 // order, one division; lane j < k writes pick j.
@@ -317,7 +350,14 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const bool vec = FULL || ((E % 4) == 0 && n == EPL);
     const size_t row = static_cast<size_t>(t) * E + e0;
 
-    float lg[EPL];
+    float lg[EPL], bs[EPL];
+    // the lane's biases, loaded with its logits (before any store)
+    if (n > 0) {
+        load_run<EPL, FULL>(bias + e0, vec, n, bs);
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) bs[i] = 0.f;
+    }
     if (n > 0) {
         if (logits_in) {
             load_run<EPL, FULL>(logits + row, vec, n, lg);
@@ -367,7 +407,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     if constexpr (kSelectFilter) {
         __shared__ FilterLds fsh;
         int pick = -1;
-        if (filter_select<EPL>(lane, e0, live, lg, bias, k, ids, w, fsh, pick)) {
+        if (filter_select<EPL>(lane, e0, live, lg, bs, k, ids, w, fsh, pick)) {
             count_pick(hist, hist_tile, E, t, k, lane, pick);
             return;
         }
@@ -375,7 +415,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     // exact keys of every expert
     uint32_t key[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) key[i] = ((live >> i) & 1u) ? ordered_key(sigmoid_rn(lg[i]) + bias[e0 + i]) : 0u;
+    for (int i = 0; i < EPL; ++i) key[i] = ((live >> i) & 1u) ? ordered_key(sigmoid_rn(lg[i]) + bs[i]) : 0u;
 
     int my_id = -1;
     float my_l = 0.f;
@@ -473,12 +513,15 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     count_pick(hist, hist_tile, E, t, k, lane, my_id);
 }
 
-// Any E: each wave stages its token's keys in its own LDS region (dynamic
+// Any E: each wave stages its token's logits in its own LDS region (dynamic
 // LDS: kSelectWaves * E * 4 bytes). A lane only touches the entries of its
-// own experts, so no barrier is needed. The picks' logits are read back from
-// the token's logit row at the end (the caller's logits, or the row this
-// wave has just written), which keeps the LDS per block at one key per
-// expert and lets four blocks share a CU at 2560 experts.
+// own experts, so no barrier is needed. The loads of a row (split partials,
+// bias) come first, with no stores among them; then the logits are written
+// out from LDS. The approximate-key filter (as filter_select, with the k-th
+// largest lane maximum as the lower bound) picks the candidates; otherwise
+// the exact keys replace the logits in LDS and k rounds pick the experts,
+// whose logits are read back from the row. One key per expert in LDS lets
+// four blocks share a CU at 2560 experts.
 __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
@@ -489,20 +532,26 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     const int wave = threadIdx.x / kWave;
     const int t = blockIdx.x * kSelectWaves + wave;
     if (t >= T) return;
-    uint32_t* keys = sel_lds + static_cast<size_t>(wave) * E;
+    uint32_t* keys = sel_lds + static_cast<size_t>(wave) * E;   // the row's logits, later (exact path) its keys
     const size_t plane = static_cast<size_t>(T) * E;
     const bool valid = token_mask[t] != 0;
-    // the lane's experts e = lane + 64 i, kLdsBatch at a time: their logits
-    // (or split partials, split by split) are all loaded before any is used,
-    // so the loads overlap; each logit still sums its splits in order
+    const int nloc = lane < E ? (E - lane + kWave - 1) / kWave : 0;   // <= 64
+    float* lrow = logits + static_cast<size_t>(t) * E;
+    uint32_t lane_top = 0u;   // the lane's largest approximate key (ordered)
+    float lane_abs = 0.f;     // and largest magnitude
+    // Pass 1, loads only (no store waits between them): the lane's experts
+    // e = lane + 64 i, kLdsBatch at a time, their logits (or split partials,
+    // split by split) all loaded before any is used; each logit still sums
+    // its splits in order. The logits stay in LDS.
 #pragma unroll 1
     for (int e0 = lane; e0 < E; e0 += kLdsBatch * kWave) {
-        float l[kLdsBatch];
+        float l[kLdsBatch], b[kLdsBatch];
 #pragma unroll
         for (int u = 0; u < kLdsBatch; ++u) {
             const int e = e0 + u * kWave;
             const size_t idx = static_cast<size_t>(t) * E + e;
             l[u] = e < E ? (logits_in ? logits[idx] : partials[idx]) : 0.f;
+            b[u] = e < E ? bias[e] : 0.f;
         }
         if (!logits_in) {
 #pragma unroll 1
@@ -517,16 +566,28 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
                 for (int u = 0; u < kLdsBatch; ++u) l[u] += q[u];
             }
 #pragma unroll
-            for (int u = 0; u < kLdsBatch; ++u) {
-                const int e = e0 + u * kWave;
-                l[u] *= scale;
-                if (e < E) logits[static_cast<size_t>(t) * E + e] = l[u];
-            }
+            for (int u = 0; u < kLdsBatch; ++u) l[u] *= scale;
         }
 #pragma unroll
         for (int u = 0; u < kLdsBatch; ++u) {
             const int e = e0 + u * kWave;
-            if (e < E) keys[e] = valid ? ordered_key(sigmoid_rn(l[u]) + bias[e]) : 0u;
+            if (e < E) {
+                keys[e] = __float_as_uint(l[u]);
+                if constexpr (kSelectFilter) {
+                    const float a = sigmoid_approx(l[u]) + b[u];
+                    lane_top = max(lane_top, ordered_key(a));
+                    lane_abs = fmaxf(lane_abs, fabsf(a));
+                }
+            }
+        }
+    }
+    // Pass 2: the logits row out (stores only)
+    if (!logits_in) {
+#pragma unroll 1
+        for (int i0 = 0; i0 < nloc; i0 += kLdsBatch) {
+#pragma unroll
+            for (int u = 0; u < kLdsBatch; ++u)
+                if (i0 + u < nloc) lrow[lane + kWave * (i0 + u)] = __uint_as_float(keys[lane + kWave * (i0 + u)]);
         }
     }
     int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
@@ -538,7 +599,61 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
         }
         return;
     }
-    const int nloc = lane < E ? (E - lane + kWave - 1) / kWave : 0;   // <= 64
+    if constexpr (kSelectFilter) {
+        // The k largest lane maxima are k distinct experts, so the k-th
+        // largest of them (a coarse lower bound of it) is at most the k-th
+        // largest approximate key A_k; cutting M below it keeps every
+        // expert that can be among the exact picks (filter_select's bound,
+        // with M's relative term taken at the largest |A| of the row). The
+        // scan recomputes each approximate key from the logit in LDS, and a
+        // candidate's logit comes from there too.
+        __shared__ FilterLds fsh;
+        const uint32_t top1[1] = {lane_top};
+        const uint32_t kth = kth_largest<1, true>(top1, 1u, k);
+        // (non-negative values order like their bit patterns)
+        const float amax = __uint_as_float(__reduce_max_sync(~0ull, __float_as_uint(lane_abs)));
+        if (kth != 0u) {
+            const float kf = key_value(kth);
+            const float lo = kf - (0x1p-15f + amax * 0x1p-20f);
+            const uint64_t below = lanemask_lt();
+            const int wv = threadIdx.x / kWave;
+            int C = 0;
+            const int nmax = (E + kWave - 1) / kWave;   // slots of lane 0, the most (the ballots need every lane)
+#pragma unroll 1
+            for (int i0 = 0; i0 < nmax; i0 += kLdsBatch) {
+                float lv[kLdsBatch], bv[kLdsBatch];
+#pragma unroll
+                for (int u = 0; u < kLdsBatch; ++u) {
+                    const bool in = i0 + u < nloc;
+                    lv[u] = in ? __uint_as_float(keys[lane + kWave * (i0 + u)]) : 0.f;
+                    bv[u] = in ? bias[lane + kWave * (i0 + u)] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < kLdsBatch; ++u) {
+                    const bool c = i0 + u < nloc && sigmoid_approx(lv[u]) + bv[u] >= lo;
+                    const uint64_t bb = __ballot(c);
+                    const int pos = C + __popcll(bb & below);
+                    if (c && pos < kWave) {
+                        fsh.cand_l[wv][pos] = lv[u];
+                        fsh.cand_b[wv][pos] = bv[u];
+                        fsh.cand_id[wv][pos] = lane + kWave * (i0 + u);
+                    }
+                    C += __popcll(bb);
+                }
+            }
+            if (C >= k && C <= kWave) {
+                const int pick = rank_candidates(lane, C, k, ids, w, fsh);
+                count_pick(hist, hist_tile, E, t, k, lane, pick);
+                return;
+            }
+        }
+    }
+    // the exact keys of every expert (in place of its logit), then the rounds
+#pragma unroll 1
+    for (int i = 0; i < nloc; ++i) {
+        const int e = lane + kWave * i;
+        keys[e] = ordered_key(sigmoid_rn(__uint_as_float(keys[e])) + bias[e]);
+    }
     uint64_t live = nloc >= 64 ? ~0ull : ((1ull << nloc) - 1);
 
     int my_id = -1;
@@ -567,10 +682,10 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
         if (lane == owner) live &= ~(1ull << (win / kWave));
         if (lane == j) my_id = static_cast<int>(win);
     }
-    // lane j < k reads pick j's logit from the row (written above by the
-    // lane that owns the expert, so the wave's stores are made visible first)
+    // lane j < k reads pick j's logit from the row (pass 2 wrote it, by the
+    // lane that owns the expert: the wave's stores are made visible first)
     __threadfence_block();
-    const float my_l = lane < k ? logits[static_cast<size_t>(t) * E + my_id] : 0.f;
+    const float my_l = lane < k ? lrow[my_id] : 0.f;
     write_picks(lane, k, my_id, my_l, ids, w);
     count_pick(hist, hist_tile, E, t, k, lane, my_id);
 }

@@ -212,7 +212,8 @@ def test_route_exact_ties_all_equal():
         np.testing.assert_array_equal(host(wt), w_o)
 
 
-@pytest.mark.parametrize("E,k", [(512, 22), (512, 11), (300, 12), (128, 16), (64, 32), (40, 13)])
+@pytest.mark.parametrize("E,k", [(512, 22), (512, 11), (300, 12), (128, 16), (64, 32), (40, 13),
+                                 (2560, 8), (1000, 22), (4096, 32)])
 def test_route_logits_in_ties_many_picks(E, k):
     """From 12 picks the selection searches the k-th largest key bit by bit
     (below, it takes k rounds): logits on a coarse grid (many exact key
@@ -264,7 +265,8 @@ def test_route_is_deterministic():
             np.testing.assert_array_equal(a, b)
 
 
-@pytest.mark.parametrize("E,k", [(64, 8), (256, 8), (256, 6), (512, 22), (300, 8), (200, 13)])
+@pytest.mark.parametrize("E,k", [(64, 8), (256, 8), (256, 6), (512, 22), (300, 8), (200, 13),
+                                 (2560, 8), (1000, 22), (4096, 32), (600, 4)])
 def test_route_logits_in_near_threshold_clusters(E, k):
     """The selection keeps only the experts whose approximate FP32 key is
     within a small margin of the k-th largest one and computes exact keys for
@@ -293,3 +295,29 @@ def test_route_logits_in_near_threshold_clusters(E, k):
     ids_o, w_o = O.route_from_logits(lg, bias, mask, k)
     np.testing.assert_array_equal(host(ids), ids_o)
     np.testing.assert_array_equal(host(wt), w_o)
+
+
+@pytest.mark.parametrize("E,k", [(256, 8), (512, 22), (2560, 8), (1000, 22)])
+def test_route_logits_in_infinite_and_nan_bias(E, k):
+    """Biases of +inf (fewer than k, k and more than k of them), -inf and NaN:
+    infinite keys tie among themselves (lowest id first), NaN keys rank below
+    every number. The approximate-key filter must hand such rows to the exact
+    selection. Bit for bit against the oracle; rows of NaN logits too."""
+    require_gpu()
+    g = np.random.default_rng(E + 7 * k)
+    T = 24
+    lg = g.standard_normal((T, E)).astype(np.float32)
+    lg[3] = np.nan
+    lg[4, ::5] = np.nan
+    mask = np.ones(T, np.uint8)
+    for n_inf in (1, k, k + 3, 0):
+        bias = (g.standard_normal(E) * 0.01).astype(np.float32)
+        cols = g.choice(E, size=n_inf + 6, replace=False)
+        bias[cols[:n_inf]] = np.inf
+        bias[cols[n_inf:n_inf + 3]] = -np.inf
+        bias[cols[n_inf + 3:]] = np.nan
+        note("route logits-in infinite/NaN bias E=%d k=%d n_inf=%d" % (E, k, n_inf))
+        _, ids, wt = m.route(None, None, dev(bias), dev(mask), k, logits=dev(lg))
+        ids_o, w_o = O.route_from_logits(lg, bias, mask, k)
+        np.testing.assert_array_equal(host(ids), ids_o, err_msg="n_inf=%d" % n_inf)
+        np.testing.assert_array_equal(host(wt), w_o, err_msg="n_inf=%d" % n_inf)
