@@ -5,13 +5,17 @@
 
 One step is one pass of the whole path over one batch of synthetic input:
 moe_route -> moe_dispatch -> moe_combine, and moe_norm_quant_nvfp4 (or
-moe_route_dispatch in place of the first two), with
+moe_route_dispatch in place of the first two, or moe_route_dispatch_quant in
+place of the first three), with
 inputs resident in HBM and every output and workspace allocated before the
 timed region. The default workload is the 8192-token prefill batch (H=8192,
 E=256, k=8, 5% invalid tokens). Prints one JSON line.
 
-Schedules (the headline is the default `auto`: the fused schedule launched
-eagerly):
+Schedules (the headline is the default `auto`: the prepare-fused schedule
+launched eagerly):
+  prepare-fused  moe_route_dispatch_quant (route, dispatch and the expert
+                 input's norm + quant in one call; the dispatch's last step
+                 and the norm + quant share one launch), then the combine
   fused          moe_route_dispatch (route and dispatch in one call, the
                  selection counting the dispatch's tile histograms), then
                  norm + quant and the combine, in order on one stream
@@ -251,17 +255,20 @@ def main():
                     help="also run a 1 GiB device copy (a plain elementwise kernel) to calibrate HBM counters")
     ap.add_argument("--no-copy-ref", dest="copy_ref", action="store_false",
                     help="skip the 1 GiB device-copy reference bandwidth")
-    ap.add_argument("--schedule", choices=["auto", "fused", "prepare", "overlap", "overlap-route", "serial"],
+    ap.add_argument("--schedule", choices=["auto", "fused", "prepare-fused", "prepare", "overlap", "overlap-route",
+                                           "serial"],
                     default="auto",
-                    help="headline schedule: route and dispatch in one call then norm+quant and combine "
+                    help="headline schedule: route, dispatch and norm+quant in one call then the combine "
+                         "(prepare-fused), route and dispatch in one call then norm+quant and combine "
                          "(fused), the four calls on one stream (serial), norm+quant on a second stream "
                          "beside the dispatch (prepare), beside dispatch + combine (overlap) or beside the "
-                         "route (overlap-route); auto = fused")
+                         "route (overlap-route); auto = prepare-fused")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline schedule from a HIP graph instead of launching it eagerly")
     ap.add_argument("--no-fc1", dest="fc1", action="store_false",
                     help="skip timing the expert FC1 (K 1024, N 2688, 512 experts, top-22)")
-    ap.add_argument("--stage", choices=["route", "dispatch", "route_dispatch", "norm_quant", "combine"],
+    ap.add_argument("--stage", choices=["route", "dispatch", "route_dispatch", "route_dispatch_quant", "norm_quant",
+                                        "combine"],
                     help="time one call of the path alone, repeated (after one fused step), then exit; "
                          "with --copy-calib also run a 1 GiB copy (for counter runs)")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -344,6 +351,11 @@ def main():
     def norm_quant_():
         m.norm_quant_nvfp4(x, qw, w.quant_gain_center, w.eps, gs, packed=packed, scales=scales)
 
+    def route_dispatch_quant_():
+        m.route_dispatch_quant(hidden, W, bias, mask, k, x, qw, w.quant_gain_center, w.eps, gs, logits=logits,
+                               topk_ids=ids, topk_w=tw, counts=counts, offsets=offsets, perm=perm, dest=dest,
+                               packed=packed, scales=scales, workspace=ws_rd)
+
     def combine_():
         m.combine(eo, slots, tw, cg, 0.0, w.eps, out=out)
 
@@ -364,6 +376,15 @@ def main():
             call()
         if ev is not None:
             ev[3].record(main)
+
+    def step_prepare_fused(ev=None):
+        main = torch.cuda.current_stream(dev)
+        for j, call in enumerate((route_dispatch_quant_, combine_)):
+            if ev is not None:
+                ev[j].record(main)
+            call()
+        if ev is not None:
+            ev[2].record(main)
 
     aux = torch.cuda.Stream(device=dev)   # default priority
 
@@ -415,7 +436,8 @@ def main():
         # first, so the dispatch and the combine see this batch's routing
         step_fused()
         call = {"route": route_, "dispatch": dispatch_, "route_dispatch": route_dispatch_,
-                "norm_quant": norm_quant_, "combine": combine_}[args.stage]
+                "route_dispatch_quant": route_dispatch_quant_, "norm_quant": norm_quant_,
+                "combine": combine_}[args.stage]
         for _ in range(args.warmup):
             call()
         st = timed(call, args.steps)
@@ -429,9 +451,9 @@ def main():
                           "copy_calib_GiB": 1 if args.copy_calib else 0}))
         return
     if args.schedule == "auto":
-        args.schedule = "fused"
+        args.schedule = "prepare-fused"
     head_step = {"prepare": step_prepare, "overlap": step_overlap, "overlap-route": step_overlap_route,
-                 "serial": step_serial, "fused": step_fused}[args.schedule]
+                 "serial": step_serial, "fused": step_fused, "prepare-fused": step_prepare_fused}[args.schedule]
     # one step on a side stream (graph capture wants the work seen once off
     # the capture stream), then the W warm-up steps on the launch stream
     # itself, eager or replayed, so that nothing first-time lands in the
@@ -460,7 +482,9 @@ def main():
                  "overlap": "norm+quant on a second stream beside dispatch + combine",
                  "overlap-route": "norm+quant on a second stream beside the route",
                  "serial": "serial",
-                 "fused": "serial, route and dispatch in one call (moe_route_dispatch)"}[args.schedule] + \
+                 "fused": "serial, route and dispatch in one call (moe_route_dispatch)",
+                 "prepare-fused": "route, dispatch and norm+quant in one call (moe_route_dispatch_quant), "
+                                  "then the combine"}[args.schedule] + \
         (", HIP graph replay" if args.graph else ", eager launches")
 
     # serial eager pass with per-call events on the launch stream (stage times)
@@ -478,6 +502,12 @@ def main():
         step_fused(fused_events[i])
     torch.cuda.synchronize()
     fused_ms = timed(step_fused, args.steps)
+    # route + dispatch + norm + quant in one call, with events
+    pf_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_prepare_fused(pf_events[i])
+    torch.cuda.synchronize()
+    prepare_fused_ms = timed(step_prepare_fused, args.steps)
     timed(step_overlap, 5)
     overlap_eager_ms = timed(step_overlap, args.steps)
     timed(step_prepare, 5)
@@ -501,6 +531,8 @@ def main():
     overlap_graph_ms = ms_per_step if args.graph and args.schedule == "overlap" else graph_ms(step_overlap)
     serial_graph_ms = ms_per_step if args.graph and args.schedule == "serial" else graph_ms(step_serial)
     fused_graph_ms = ms_per_step if args.graph and args.schedule == "fused" else graph_ms(step_fused)
+    prepare_fused_graph_ms = (ms_per_step if args.graph and args.schedule == "prepare-fused"
+                              else graph_ms(step_prepare_fused))
 
     # cold: flush the 256 MB last-level cache (a 512 MiB write) before each step
     cold_ms = None
@@ -565,6 +597,12 @@ def main():
     stages["route_dispatch"] = {"ms": round(rd_ms, 4), "bytes": rd_bytes,
                                 "GBps": round(rd_bytes / (rd_ms * 1e-3) / 1e9, 1),
                                 "note": "moe_route_dispatch: the fused call, from the fused pass"}
+    rdq_ms = float(np.mean([pf_events[i][0].elapsed_time(pf_events[i][1]) for i in range(args.steps)]))
+    rdq_bytes = rd_bytes + nbytes["norm_quant"]
+    stages["route_dispatch_quant"] = {"ms": round(rdq_ms, 4), "bytes": rdq_bytes,
+                                      "GBps": round(rdq_bytes / (rdq_ms * 1e-3) / 1e9, 1),
+                                      "note": "moe_route_dispatch_quant: route, dispatch and norm + quant in "
+                                              "one call, from its own pass"}
 
     comb_gbs = nbytes["combine"] / (stage_ms["combine"] * 1e-3) / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
@@ -613,6 +651,8 @@ def main():
         "schedules": {"headline": head_name, "headline_ms": round(ms_per_step, 4),
                       "serial_eager_ms": round(serial_ms, 4), "fused_eager_ms": round(fused_ms, 4),
                       "fused_graph_ms": round(fused_graph_ms, 4),
+                      "prepare_fused_eager_ms": round(prepare_fused_ms, 4),
+                      "prepare_fused_graph_ms": round(prepare_fused_graph_ms, 4),
                       "prepare_eager_ms": round(prepare_eager_ms, 4),
                       "overlap_eager_ms": round(overlap_eager_ms, 4),
                       "overlap_route_eager_ms": round(overlap_route_ms, 4),

@@ -13,6 +13,9 @@
  *                         for callers that cannot allocate)
  *   moe_route_dispatch    moe_route followed by moe_dispatch in one call, the
  *                         selection counting the dispatch's tile histograms
+ *                         (moe_route_dispatch_quant: and moe_norm_quant_nvfp4
+ *                         of the expert input, the dispatch's last step and
+ *                         the norm + quant sharing one launch)
  *   moe_norm_quant_nvfp4  RMSNorm of the expert input with one BF16 rounding,
  *                         fused with NVFP4 quantisation (E2M1 codes, E4M3
  *                         block-16 scales, static global scale); the
@@ -187,6 +190,34 @@ int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, con
                        float* logits, int32_t* topk_ids, float* topk_w,
                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_dispatch_quant — moe_route_dispatch, then moe_norm_quant_nvfp4 of
+ * the expert input, in one call: what the experts need of a batch.
+ *
+ * TensorRT-LLM PR #21356, "Where they plug in": the expert input's norm and
+ * quantisation run beside the routing (on an auxiliary stream there). Here
+ * the dispatch's place step and the norm + quant share one launch, blocks of
+ * each side by side, when x's rows fill whole blocks of the staged norm +
+ * quant (H / 16 = 256, 512, 768 or 1024) and there are more tokens than its
+ * blocks; otherwise they run one after the other. Same outputs either way:
+ * every output is bit-identical to moe_route_dispatch followed by
+ * moe_norm_quant_nvfp4.
+ *
+ * Arguments: those of moe_route_dispatch, then those of moe_norm_quant_nvfp4
+ * for x [T,H] BF16 (the expert input; the same T and H as hidden, contiguous
+ * rows): norm_w [H] FP32, gain_center, eps, global_scale (one FP32 on the
+ * device), packed [T,H/2], scales [T,H/16]. workspace: at least
+ * moe_route_dispatch_workspace_bytes(T, H, E, k, hidden_dtype, logits_in).
+ * Errors: those of either call.
+ */
+int moe_route_dispatch_quant(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                             const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+                             float* logits, int32_t* topk_ids, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
+                             const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                             const float* global_scale, uint8_t* packed, uint8_t* scales,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_dispatch_noalloc — moe_dispatch without a workspace argument, for

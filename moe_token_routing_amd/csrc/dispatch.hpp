@@ -31,4 +31,22 @@ int run_clear(int32_t* p, long long n, void* stream);
 int run_place(const int32_t* topk_ids, long long n, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
               int32_t* dest, int32_t* tile_counts, void* stream);
 
+// The place step's form for n slots over E experts (a PlaceMode of
+// place.hpp: 0 after a separate column scan, 1 summing the tile histograms
+// itself, 2 one tile), and that column scan.
+int place_mode(long long n, int E);
+int run_scan(int32_t* tile_counts, long long n, int E, int32_t* counts, void* stream);
+
+// moe_norm_quant_nvfp4's argument checks (contiguous input), before any launch.
+int check_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                     const float* global_scale, int T, int H, const uint8_t* packed, const uint8_t* scales);
+
+// run_place, then moe_norm_quant_nvfp4 of x [T,H]: in one launch when the
+// shapes allow (blocks of the place step beside blocks of the staged norm +
+// quant), else one after the other. Same outputs either way.
+int run_place_norm_quant(const int32_t* topk_ids, long long n, int E, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* dest, int32_t* tile_counts, const uint16_t* x,
+                         const float* norm_w, float gain_center, float eps, const float* global_scale, int T, int H,
+                         uint8_t* packed, uint8_t* scales, void* stream);
+
 }  // namespace moe

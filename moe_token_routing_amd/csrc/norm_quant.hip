@@ -36,16 +36,14 @@
 // copies in flight. Same arithmetic, same order.
 #include <cmath>
 
+#include "dispatch.hpp"
 #include "launch.hpp"
 #include "nvfp4.hpp"
+#include "place.hpp"
 #include "rows.hpp"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ float round_to_bf16(float f) {
-    return __uint_as_float(f32_to_bf16_rne(f) << 16);
-}
 
 // RN to BF16 of an FP32 value, returned as the FP32 value it represents
 // (one v_cvt_pk_bf16_f32 with a zero low half; v must not be NaN).
@@ -280,10 +278,12 @@ __device__ __forceinline__ void barrier_lds() {
 // this one is reduced and quantised. stage[2i + j][thread] holds vector j of
 // the thread's block i; a wave's copies write only its own 64 slots of each
 // row, which it alone reads back.
+// (the kernel's body as a device function of its block index `blk` among
+// `nblocks`, so that it can also run beside other work in one launch)
 template <int BPT, int TPT>
-__global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
-    const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
-    const float* __restrict__ global_scale, int T, int H, int shard8,
+__device__ __forceinline__ void norm_quant_staged_body(
+    int blk, int nblocks, const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center,
+    float eps, const float* __restrict__ global_scale, int T, int H, int shard8,
     uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     static_assert(TPT == kWave || TPT == kRowBlock, "whole waves or the whole block per token");
     __shared__ float red[2][kRowBlock / kWave];
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
         load_gains(norm_w, b, gain_center, gain[i]);
     }
     const bool gok = gains_finite<BPT>(gain);
-    const int step = gridDim.x * tokens_per_block;
-    int t = blockIdx.x * tokens_per_block + sub;
+    const int step = nblocks * tokens_per_block;
+    int t = blk * tokens_per_block + sub;
     if (t < T) {
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
     }
     int par = 0;
     // block-uniform trip count (every wave reaches every barrier)
-    for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += step, t += step, par ^= 1) {
+    for (int t0 = blk * tokens_per_block; t0 < T; t0 += step, t += step, par ^= 1) {
         // uniform in the wave; with one token per block always true here
         const bool tok_ok = TPT == kRowBlock || t < T;
         wait_copies();
@@ -376,6 +376,38 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
     }
 }
 
+template <int BPT, int TPT>
+__global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
+    const float* __restrict__ global_scale, int T, int H, int shard8,
+    uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
+    norm_quant_staged_body<BPT, TPT>(blockIdx.x, gridDim.x, x, norm_w, gain_center, eps, global_scale, T, H,
+                                     shard8, packed, scales);
+}
+
+// The dispatch's place step and norm + quant in one launch: blocks below
+// n_place place their tile of slots (place_body), the others run the
+// staged norm + quant over the tokens. The two depend on nothing of each
+// other, and the place step's few latency-bound blocks then run beside the
+// bandwidth-bound norm + quant instead of before it, with no second stream
+// to fork and join (TensorRT-LLM PR #21356, "Where they plug in": the
+// expert input prepared beside the routing).
+template <int MODE, int BPT>
+__global__ __launch_bounds__(kRowBlock) void place_norm_quant_kernel(
+    int n_place, const int32_t* __restrict__ ids, int n, int E, int tile, int tiles,
+    const int32_t* __restrict__ tile_hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ dest, const u32x4* __restrict__ x,
+    const float* __restrict__ norm_w, float gain_center, float eps, const float* __restrict__ global_scale,
+    int T, int H, uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
+    static_assert(kDispBlock == kRowBlock, "one block size");
+    extern __shared__ __attribute__((aligned(16))) int32_t place_lds[];
+    if (static_cast<int>(blockIdx.x) < n_place)
+        place_body<MODE>(blockIdx.x, place_lds, ids, n, E, tile, tiles, tile_hist, counts, offsets, perm, dest);
+    else
+        norm_quant_staged_body<BPT, kRowBlock>(blockIdx.x - n_place, gridDim.x - n_place, x, norm_w, gain_center,
+                                               eps, global_scale, T, H, H / 8, packed, scales);
+}
+
 struct BlockGeom {
     int tpt;   // threads per token (power of two, <= 256)
     int bpt;   // 16-element blocks per thread
@@ -414,6 +446,87 @@ int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center,
 }
 
 }  // namespace
+}  // namespace moe
+
+namespace moe {
+
+int check_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                     const float* global_scale, int T, int H, const uint8_t* packed, const uint8_t* scales) {
+    if (T < 0 || H < 16 || H > MOE_MAX_HIDDEN || H % 16 != 0) return MOE_ERR_BAD_SHAPE;
+    if (!std::isfinite(gain_center) || !std::isfinite(eps) || eps < 0.f) return MOE_ERR_BAD_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !norm_w || !global_scale || !packed || !scales) return MOE_ERR_NULL_ARG;
+    if (!all_aligned16(x, norm_w, packed, scales)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+namespace {
+
+template <int MODE, int BPT>
+int launch_place_norm_quant(int grid, int n_place, size_t lds, const int32_t* topk_ids, int n, int E, int tile,
+                            int tiles, int32_t* tile_counts, int32_t* counts, int32_t* offsets, int32_t* perm,
+                            int32_t* dest, const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                            const float* global_scale, int T, int H, uint8_t* packed, uint8_t* scales,
+                            void* stream) {
+    return launch(place_norm_quant_kernel<MODE, BPT>, dim3(grid), dim3(kRowBlock), lds, stream, n_place, topk_ids,
+                  n, E, tile, tiles, static_cast<const int32_t*>(tile_counts), counts, offsets, perm, dest,
+                  reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
+                  reinterpret_cast<uint2*>(packed), scales);
+}
+
+template <int MODE>
+int resident_place_norm_quant(int bpt, size_t lds) {
+    switch (bpt) {
+        case 1: return resident_blocks(place_norm_quant_kernel<MODE, 1>, kRowBlock, lds);
+        case 2: return resident_blocks(place_norm_quant_kernel<MODE, 2>, kRowBlock, lds);
+        case 3: return resident_blocks(place_norm_quant_kernel<MODE, 3>, kRowBlock, lds);
+        default: return resident_blocks(place_norm_quant_kernel<MODE, 4>, kRowBlock, lds);
+    }
+}
+
+}  // namespace
+
+int run_place_norm_quant(const int32_t* topk_ids, long long n, int E, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* dest, int32_t* tile_counts, const uint16_t* x,
+                         const float* norm_w, float gain_center, float eps, const float* global_scale, int T, int H,
+                         uint8_t* packed, uint8_t* scales, void* stream) {
+    const BlockGeom geo = block_geom(H);
+    // the fused launch covers the staged norm + quant with one token per
+    // block (H / 16 = 256 BPT) when every one of its blocks gets several
+    // tokens, as the staged kernel is meant for
+    const bool whole = geo.tpt == kRowBlock && H / 16 == geo.bpt * kRowBlock && geo.bpt <= 4;
+    if (whole && n > 0 && T > 0) {
+        const int mode = place_mode(n, E);
+        const DispatchTiles d = dispatch_tiles(n);
+        const int n_place = mode == kPlaceSingle ? 1 : d.tiles;
+        const size_t lds = place_lds_bytes(mode, E);
+        const int per_cu = mode == kPlaceSingle ? resident_place_norm_quant<kPlaceSingle>(geo.bpt, lds)
+                           : mode == kPlaceFused ? resident_place_norm_quant<kPlaceFused>(geo.bpt, lds)
+                                                 : resident_place_norm_quant<kPlaceScanned>(geo.bpt, lds);
+        const int grid = device_cu_count() * per_cu;   // every block resident at once
+        const int n_nq = grid - n_place;
+        if (n_nq >= device_cu_count() && T > n_nq) {
+            if (mode == kPlaceScanned) {
+                const int rc = run_scan(tile_counts, n, E, counts, stream);
+                if (rc) return rc;
+            }
+#define MOE_PNQ(M, B)                                                                                         \
+    if (mode == M && geo.bpt == B)                                                                            \
+        return launch_place_norm_quant<M, B>(grid, n_place, lds, topk_ids, static_cast<int>(n), E, d.tile, d.tiles, \
+                                             tile_counts, counts, offsets, perm, dest, x, norm_w, gain_center, eps, \
+                                             global_scale, T, H, packed, scales, stream);
+            MOE_PNQ(kPlaceSingle, 1) MOE_PNQ(kPlaceSingle, 2) MOE_PNQ(kPlaceSingle, 3) MOE_PNQ(kPlaceSingle, 4)
+            MOE_PNQ(kPlaceFused, 1) MOE_PNQ(kPlaceFused, 2) MOE_PNQ(kPlaceFused, 3) MOE_PNQ(kPlaceFused, 4)
+            MOE_PNQ(kPlaceScanned, 1) MOE_PNQ(kPlaceScanned, 2) MOE_PNQ(kPlaceScanned, 3) MOE_PNQ(kPlaceScanned, 4)
+#undef MOE_PNQ
+        }
+    }
+    int rc = n > 0 ? run_place(topk_ids, n, E, counts, offsets, perm, dest, tile_counts, stream)
+                   : run_dispatch_empty(counts, offsets, E, stream);
+    if (rc) return rc;
+    return moe_norm_quant_nvfp4(x, norm_w, gain_center, eps, global_scale, T, H, packed, scales, stream);
+}
+
 }  // namespace moe
 
 extern "C" int moe_norm_quant_nvfp4_rank_block(const uint16_t* x, int shard, const float* norm_w,

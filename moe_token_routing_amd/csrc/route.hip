@@ -734,16 +734,17 @@ extern "C" size_t moe_route_dispatch_workspace_bytes(int T, int H, int E, int k,
     return round256(moe_route_workspace_bytes(T, H, E, k, hidden_dtype, logits_in)) + fused_hist_bytes(T, k, E);
 }
 
-extern "C" int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, const float* bias,
-                                  const uint8_t* token_mask, float scale, int T, int H, int E, int k,
-                                  float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
-                                  int32_t* offsets, int32_t* perm, int32_t* dest, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-    using namespace moe;
-    int rc = check_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w);
-    if (rc) return rc;
-    rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
-    if (rc) return rc;
+namespace moe {
+namespace {
+
+// The steps of moe_route_dispatch and moe_route_dispatch_quant (x == nullptr:
+// no norm + quant) after their own argument checks.
+int route_dispatch_run(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                       const uint8_t* token_mask, float scale, int T, int H, int E, int k, float* logits,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* dest, const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                       const float* global_scale, uint8_t* packed, uint8_t* scales, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     if (T == 0) return run_dispatch_empty(counts, offsets, E, stream);
     const size_t route_bytes = round256(moe_route_workspace_bytes(T, H, E, k, hidden_dtype, hidden == nullptr));
     const size_t hist_bytes = fused_hist_bytes(T, k, E);
@@ -754,8 +755,47 @@ extern "C" int moe_route_dispatch(const void* hidden, int hidden_dtype, const fl
     const long long n = static_cast<long long>(T) * k;
     const DispatchTiles d = dispatch_tiles(n);
     int32_t* hist = hist_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + route_bytes) : nullptr;
-    rc = run_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
-                   workspace, hist, static_cast<long long>(d.tiles) * E, d.tile, stream);
+    const int rc = run_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
+                             workspace, hist, static_cast<long long>(d.tiles) * E, d.tile, stream);
     if (rc) return rc;
-    return run_place(topk_ids, n, E, counts, offsets, perm, dest, hist, stream);
+    if (!x) return run_place(topk_ids, n, E, counts, offsets, perm, dest, hist, stream);
+    return run_place_norm_quant(topk_ids, n, E, counts, offsets, perm, dest, hist, x, norm_w, gain_center, eps,
+                                global_scale, T, H, packed, scales, stream);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                                  const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+                                  float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, int32_t* dest, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    int rc = check_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w);
+    if (rc) return rc;
+    rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
+    if (rc) return rc;
+    return route_dispatch_run(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
+                              counts, offsets, perm, dest, nullptr, nullptr, 0.f, 0.f, nullptr, nullptr, nullptr,
+                              workspace, workspace_bytes, stream);
+}
+
+extern "C" int moe_route_dispatch_quant(const void* hidden, int hidden_dtype, const float* W, const float* bias,
+                                        const uint8_t* token_mask, float scale, int T, int H, int E, int k,
+                                        float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                        int32_t* offsets, int32_t* perm, int32_t* dest, const uint16_t* x,
+                                        const float* norm_w, float gain_center, float eps,
+                                        const float* global_scale, uint8_t* packed, uint8_t* scales,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    int rc = check_route(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w);
+    if (rc) return rc;
+    rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
+    if (rc) return rc;
+    rc = check_norm_quant(x, norm_w, gain_center, eps, global_scale, T, H, packed, scales);
+    if (rc) return rc;
+    return route_dispatch_run(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
+                              counts, offsets, perm, dest, x, norm_w, gain_center, eps, global_scale, packed, scales,
+                              workspace, workspace_bytes, stream);
 }

@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"moe_status_string", "moe_route_workspace_bytes", "moe_route",
                           "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_dispatch_noalloc",
-                          "moe_route_dispatch_workspace_bytes", "moe_route_dispatch",
+                          "moe_route_dispatch_workspace_bytes", "moe_route_dispatch", "moe_route_dispatch_quant",
                           "moe_norm_quant_nvfp4",
                           "moe_norm_quant_nvfp4_rank_block", "moe_combine",
                           "moe_expert_fc1_workspace_bytes", "moe_expert_fc1_nvfp4",
@@ -143,6 +143,21 @@ def test_route_dispatch_rejects_before_launch(lib):
     assert m.route_dispatch_workspace_bytes(200, 16, 16, 4, m.MOE_DTYPE_BF16, logits_in=True) == 0
     assert m.route_dispatch_workspace_bytes(2000, 16, 16, 4, m.MOE_DTYPE_BF16, logits_in=True) == \
         m.dispatch_workspace_bytes(2000, 4, 16) > 0
+
+
+def test_route_dispatch_quant_rejects_before_launch(lib):
+    f = lib.moe_route_dispatch_quant
+
+    def call(hidden=FAKE, W=FAKE, T=4, H=64, E=16, k=4, counts=FAKE, x=FAKE, nw=FAKE, gc=1.0, eps=1e-6, gs=FAKE,
+             packed=FAKE, scales=FAKE, ws=FAKE, wsb=1 << 30):
+        return f(hidden, 1, W, FAKE, FAKE, 1.0, T, H, E, k, FAKE, FAKE, FAKE, counts, FAKE, FAKE, FAKE,
+                 x, nw, gc, eps, gs, packed, scales, ws, wsb, None)
+
+    assert call(k=17) == -2 and call(H=24) == -2 and call(counts=None) == -1     # route, dispatch
+    assert call(x=None) == -1 and call(gs=None) == -1 and call(packed=None) == -1  # norm + quant
+    assert call(eps=-1.0) == -5 and call(gc=float("nan")) == -5
+    assert call(x=V((1 << 20) + 2)) == -7
+    assert call(ws=None) == -4
 
 
 def test_dispatch_rejects_before_launch(lib):

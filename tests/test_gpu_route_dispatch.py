@@ -1,6 +1,8 @@
 """moe_route_dispatch (the route and the dispatch in one call, the selection
 counting the dispatch's tile histograms) against the two separate calls and
-the oracle.
+the oracle; moe_route_dispatch_quant (and the norm + quant of the expert
+input, sharing a launch with the dispatch's last step) against
+moe_route_dispatch followed by moe_norm_quant_nvfp4.
 
 Every output -- logits, ids, weights, counts, offsets, perm, dest -- must be
 bit-identical to moe_route followed by moe_dispatch on the same inputs, and
@@ -175,3 +177,90 @@ def test_route_dispatch_graph_replay(name):
         ref = O.dispatch(replayed[1], w.E)
         for n, g, r in zip(NAMES[3:], replayed[3:], ref):
             np.testing.assert_array_equal(g, r, err_msg="replay %d: %s vs oracle" % (rep, n))
+
+
+NQ_NAMES = NAMES + ("packed", "scales")
+
+
+def _quant_inputs(w, T, H):
+    g = np.random.default_rng(T + H)
+    x = wl.f32_to_bf16_bits((g.standard_normal((T, H)) * 0.7).astype(np.float32))
+    nw = (g.standard_normal(H) * 0.05).astype(np.float32)
+    return x, nw
+
+
+# prefill (8192 and 3000 tokens) and large E (H 4096) take the one-launch
+# path (the latter after the separate column scan); decode (too few tokens),
+# wide top-22 (H 1024) and tiny (one tile, H 256) run the two steps in turn.
+@pytest.mark.parametrize("name,T", [("prefill", None), ("prefill", 3000), ("large_e", None), ("decode", None),
+                                    ("wide_k", 2000), ("tiny", None)])
+def test_route_dispatch_quant_matches_separate_calls(name, T):
+    require_gpu()
+    w = wl.WORKLOADS[name]
+    T = w.T if T is None else T
+    note("route_dispatch_quant %s T=%d" % (name, T))
+    hidden = wl.hidden(w, T)
+    H = hidden.shape[1]
+    x, nw = _quant_inputs(w, T, H)
+    h_d, W_d, b_d, m_d = dev(hidden), dev(wl.router_weight(w)), dev(wl.bias(w)), dev(wl.token_mask(w, T))
+    x_d, nw_d = dev(x), dev(nw)
+    gs = torch.tensor([345.44577], dtype=torch.float32, device=DEV)
+    fus = [host(t) for t in m.route_dispatch_quant(h_d, W_d, b_d, m_d, w.k, x_d, nw_d, 1.0, 1e-6, gs)]
+    sep = [host(t) for t in m.route_dispatch(h_d, W_d, b_d, m_d, w.k)]
+    sep += [host(t) for t in m.norm_quant_nvfp4(x_d, nw_d, 1.0, 1e-6, gs)]
+    torch.cuda.synchronize()
+    for n_, a, b in zip(NQ_NAMES, fus, sep):
+        np.testing.assert_array_equal(a, b, err_msg="%s T=%d: %s" % (name, T, n_))
+
+
+def test_route_dispatch_quant_graph_replay():
+    """The one-launch path captured in a graph and replayed with new inputs:
+    every replay equals the separate eager calls."""
+    require_gpu()
+    w = wl.WORKLOADS["prefill"]
+    T, H = w.T, w.H
+    h_d = dev(wl.hidden(w, T))
+    W_d, b_d, m_d = dev(wl.router_weight(w)), dev(wl.bias(w)), dev(wl.token_mask(w, T))
+    x, nw = _quant_inputs(w, T, H)
+    x_d, nw_d = dev(x), dev(nw)
+    gs = torch.tensor([345.44577], dtype=torch.float32, device=DEV)
+    outs = dict(logits=torch.empty((T, w.E), dtype=torch.float32, device=DEV),
+                topk_ids=torch.empty((T, w.k), dtype=torch.int32, device=DEV),
+                topk_w=torch.empty((T, w.k), dtype=torch.float32, device=DEV),
+                counts=torch.empty(w.E, dtype=torch.int32, device=DEV),
+                offsets=torch.empty(w.E + 1, dtype=torch.int32, device=DEV),
+                perm=torch.empty(T * w.k, dtype=torch.int32, device=DEV),
+                dest=torch.empty(T * w.k, dtype=torch.int32, device=DEV),
+                packed=torch.empty((T, H // 2), dtype=torch.uint8, device=DEV),
+                scales=torch.empty((T, H // 16), dtype=torch.uint8, device=DEV))
+    ws = torch.empty(m.route_dispatch_workspace_bytes(T, H, w.E, w.k, m.MOE_DTYPE_BF16), dtype=torch.uint8,
+                     device=DEV)
+
+    def call():
+        m.route_dispatch_quant(h_d, W_d, b_d, m_d, w.k, x_d, nw_d, 1.0, 1e-6, gs, workspace=ws, **outs)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        note("route_dispatch_quant graph replay %d" % rep)
+        gt = torch.Generator(device=DEV).manual_seed(60 + rep)
+        h_d.copy_(torch.randn((T, H), generator=gt, device=DEV).to(torch.bfloat16))
+        x_d.copy_(torch.randn((T, H), generator=gt, device=DEV).to(torch.bfloat16))
+        m_d.copy_((torch.rand(T, generator=gt, device=DEV) > 0.2).to(torch.uint8))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = [host(outs[n_]).copy() for n_ in NQ_NAMES]
+        sep = [host(t) for t in m.route_dispatch(h_d, W_d, b_d, m_d, w.k)]
+        sep += [host(t) for t in m.norm_quant_nvfp4(x_d, nw_d, 1.0, 1e-6, gs)]
+        torch.cuda.synchronize()
+        for n_, a, b in zip(NQ_NAMES, replayed, sep):
+            np.testing.assert_array_equal(a, b, err_msg="replay %d: %s" % (rep, n_))
