@@ -487,7 +487,12 @@ def main():
                                   "then the combine"}[args.schedule] + \
         (", HIP graph replay" if args.graph else ", eager launches")
 
-    # serial eager pass with per-call events on the launch stream (stage times)
+    # serial eager pass with per-call events on the launch stream (stage times);
+    # each schedule's kernels run once untimed first, so no first launch in
+    # the process (its code-object load) falls inside the events
+    for warm in (step_serial, step_fused, step_prepare_fused):
+        warm()
+    torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
