@@ -322,11 +322,16 @@ __device__ __forceinline__ void norm_quant_staged_body(
         }
     }
     int par = 0;
-    // block-uniform trip count (every wave reaches every barrier)
+    wait_copies();
+    // block-uniform trip count (every wave reaches every barrier). Each
+    // token's row has landed when its iteration starts: the wait for it
+    // comes before the previous token's stores, so no iteration waits for
+    // its predecessor's stores (the vector memory counter covers stores
+    // too, and loads and stores may complete out of order against each
+    // other, so the wait cannot single out the copies).
     for (int t0 = blk * tokens_per_block; t0 < T; t0 += step, t += step, par ^= 1) {
         // uniform in the wave; with one token per block always true here
         const bool tok_ok = TPT == kRowBlock || t < T;
-        wait_copies();
         uint32_t xw[BPT][8];
         float ss = 0.f;
         if (tok_ok) {
@@ -361,17 +366,24 @@ __device__ __forceinline__ void norm_quant_staged_body(
 #pragma unroll
             for (int w = 1; w < kRowBlock / kWave; ++w) ss += red[par][w];
         }
+        // (a wave with no token issued no copies: nothing to wait for)
         if (!tok_ok) continue;
         const float rinv = rms_inverse(ss, H, hf, inv_h, eps);
         const bool finite = gok && ss <= 3.40282347e38f && rinv <= 3.40282347e38f;
+        uint2 codes[BPT];
+        uint32_t sf[BPT];
+#pragma unroll
+        for (int i = 0; i < BPT; ++i)
+            codes[i] = finite ? encode_block<true>(xw[i], gain[i], rinv, gs, outs_of, &sf[i])
+                              : encode_block<false>(xw[i], gain[i], rinv, gs, outs_of, &sf[i]);
+        // the next token's row has landed (its copies were issued before
+        // this token's reduction); then this token's stores
+        wait_copies();
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             const int b = tid + i * TPT;
-            uint32_t sf;
-            const uint2 codes = finite ? encode_block<true>(xw[i], gain[i], rinv, gs, outs_of, &sf)
-                                       : encode_block<false>(xw[i], gain[i], rinv, gs, outs_of, &sf);
-            packed[static_cast<size_t>(t) * nblk + b] = codes;
-            scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf);
+            packed[static_cast<size_t>(t) * nblk + b] = codes[i];
+            scales[static_cast<size_t>(t) * nblk + b] = static_cast<uint8_t>(sf[i]);
         }
     }
 }

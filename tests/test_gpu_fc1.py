@@ -346,3 +346,83 @@ def test_fc1_fed_by_the_pre_expert_quantiser(swiglu):
     near = near_fn(*args)
     nset, nmis = _check(host(yp_d), host(ys_d), ref_p, ref_s, near, "fc1 chain")
     print("chain swiglu=%s: boundary blocks %d of %d, mismatches inside %d" % (swiglu, nset, near.size, nmis))
+
+
+# ---- inputs whose every partial sum is exact in FP32 ----------------------
+
+_POW2_E4M3 = np.array([0x30, 0x38, 0x40], dtype=np.uint8)   # 0.5, 1, 2
+
+
+def _case_dyadic(T, k, E, K, N, seed, invalid=0.0, skew=None, gx=4.0, gw_exp=(-2, 2)):
+    """Uniform E2M1 codes with power-of-two block scales (E4M3 0.5, 1, 2) and
+    power-of-two global scales: every dequantised element is a multiple of
+    2^-2, every product of 2^-4, and while the sum of |products| stays below
+    2^20 every partial sum, in any order and grouping, is a multiple of 2^-4
+    below 2^20, so an FP32 accumulation rounds nowhere and alpha, a power of
+    two, is exact too. The test asserts that premise on the drawn data."""
+    g = np.random.default_rng(seed)
+    xp = g.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
+    xs = _POW2_E4M3[g.integers(0, 3, size=(T, K // 16))]
+    wp = g.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = _POW2_E4M3[g.integers(0, 3, size=(E, N, K // 16))]
+    gw = (2.0 ** g.integers(gw_exp[0], gw_exp[1] + 1, size=E)).astype(np.float32)
+    gx = np.float32(gx)
+    perm, offsets = _routing(g, T, k, E, invalid, skew)
+    acc, mag = O.fc1_exact(xp, xs, gx, perm, offsets, k, wp, ws, gw)
+    # undo alpha = 1 / (gs_x gs_w[e]) row by row: the kernel's raw sums
+    used = int(offsets[-1])
+    gw_row = np.zeros(len(perm))
+    for e in range(E):
+        gw_row[offsets[e]:offsets[e + 1]] = gw[e]
+    raw_scale = (float(gx) * gw_row)[:, None]
+    raw, raw_mag = acc * raw_scale, mag * raw_scale
+    assert raw_mag[:used].max() * 16 < 2.0 ** 24, "premise: partial sums exact in FP32"
+    assert np.array_equal(raw * 16, np.round(raw * 16)), "premise: multiples of 2^-4"
+    return (xp, xs, gx, perm, offsets, k, wp, ws, gw), acc
+
+
+@pytest.mark.parametrize("T,k,E,K,N,invalid,skew", [
+    (9, 2, 2, 16384, 128, 0.0, None),           # the largest K: 256 stages, 32 scale chunks
+    (300, 4, 8, 1024, 384, 0.05, [6, 0, 1, 1, 3, 1, 1, 2]),   # row tiles over experts, an empty one
+    (37, 3, 5, 2048, 2688, 0.1, None),          # the FC1 workload's N: 14 column tiles
+])
+def test_fc1_dyadic_inputs_bit_exact(T, k, E, K, N, invalid, skew):
+    """With exact accumulation the only rounding left is the square's (once,
+    like the oracle's), so codes and scales must match on every block."""
+    base, acc = _case_dyadic(T, k, E, K, N, seed=1000 + K, invalid=invalid, skew=skew)
+    gy = O.global_scale(O.relu2(acc))
+    args = base + (gy,)
+    got_p, got_s = _run(*args, "dyadic")
+    ref_p, ref_s = O.expert_fc1_nvfp4(*args)
+    used = int(args[4][-1])
+    assert np.array_equal(got_s, ref_s), "dyadic inputs: scale mismatch"
+    assert np.array_equal(got_p, ref_p), "dyadic inputs: code mismatch"
+    generic = O.fc1_boundary_blocks(*args)
+    print("bit-exact on all %d blocks (the generic FP32 boundary set would excuse %d)"
+          % (used * (N // 16), int(generic.sum())))
+
+
+@pytest.mark.parametrize("T,k,E,K,N,invalid,gx", [
+    (9, 2, 2, 16384, 64, 0.0, 128.0),
+    (300, 4, 8, 1024, 192, 0.05, 32.0),
+    (37, 3, 5, 2048, 1344, 0.1, 64.0),
+])
+def test_fc1_swiglu_dyadic_inputs(T, k, E, K, N, invalid, gx):
+    """SwiGLU on the same exact-accumulation inputs: the gate and up values
+    are exact, so the boundary set needs only the FP32 silu(g) u evaluation's
+    error (no accumulation roundings). The global scales keep the gates
+    within +-80, where silu stays a normal FP32 number, so no element is
+    excused for an underflow."""
+    base, acc = _case_dyadic(T, k, E, K, 2 * N, seed=2000 + K, invalid=invalid, gx=gx, gw_exp=(0, 2))
+    assert np.abs(acc[:, :N]).max() < 80.0, "premise: gates within silu's normal range"
+    gy = O.global_scale(_swiglu_values(acc))
+    args = base + (gy,)
+    got_p, got_s = _run_swiglu(*args, "dyadic")
+    ref_p, ref_s = O.expert_fc1_swiglu_nvfp4(*args)
+    near = O.fc1_swiglu_boundary_blocks(*args, adds=0)
+    nset, nmis = _check(got_p, got_s, ref_p, ref_s, near, "fc1 swiglu dyadic")
+    used = int(args[4][-1])
+    assert not got_p[used:].any() and not got_s[used:].any()
+    generic = O.fc1_swiglu_boundary_blocks(*args)
+    print("boundary blocks %d of %d with exact sums (generic set %d), mismatches inside %d"
+          % (nset, used * (N // 16), int(generic.sum()), nmis))
