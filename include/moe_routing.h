@@ -199,23 +199,25 @@ int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, con
  * quantisation run beside the routing (on an auxiliary stream there). Here
  * the dispatch's place step and the norm + quant share one launch, blocks of
  * each side by side, when x's rows fill whole blocks of the staged norm +
- * quant (H / 16 = 256, 512, 768 or 1024) and there are more tokens than its
+ * quant (Hq / 16 = 256, 512, 768 or 1024) and there are more tokens than its
  * blocks; otherwise they run one after the other. Same outputs either way:
  * every output is bit-identical to moe_route_dispatch followed by
  * moe_norm_quant_nvfp4.
  *
  * Arguments: those of moe_route_dispatch, then those of moe_norm_quant_nvfp4
- * for x [T,H] BF16 (the expert input; the same T and H as hidden, contiguous
- * rows): norm_w [H] FP32, gain_center, eps, global_scale (one FP32 on the
- * device), packed [T,H/2], scales [T,H/16]. workspace: at least
- * moe_route_dispatch_workspace_bytes(T, H, E, k, hidden_dtype, logits_in).
- * Errors: those of either call.
+ * for the expert input x [T,Hq] BF16 (the same T as hidden; its own width
+ * Hq, since the experts may read a narrower stream than the router, e.g. a
+ * pooled one; contiguous rows): norm_w [Hq] FP32, gain_center, eps,
+ * global_scale (one FP32 on the device), packed [T,Hq/2], scales [T,Hq/16].
+ * workspace: at least moe_route_dispatch_workspace_bytes(T, H, E, k,
+ * hidden_dtype, logits_in). Errors: those of either call (Hq checked as
+ * moe_norm_quant_nvfp4 checks H).
  */
 int moe_route_dispatch_quant(const void* hidden, int hidden_dtype, const float* W, const float* bias,
                              const uint8_t* token_mask, float scale, int T, int H, int E, int k,
                              float* logits, int32_t* topk_ids, float* topk_w,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* dest,
-                             const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                             const uint16_t* x, int Hq, const float* norm_w, float gain_center, float eps,
                              const float* global_scale, uint8_t* packed, uint8_t* scales,
                              void* workspace, size_t workspace_bytes, void* stream);
 

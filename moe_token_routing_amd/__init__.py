@@ -43,7 +43,7 @@ _SIGNATURES = {
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_route_dispatch_quant": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_float, _c_int, _c_int, _c_int, _c_int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                          _vp, _vp, _c_float, _c_float, _vp, _vp, _vp, _vp, _c_size, _vp]),
+                                          _vp, _c_int, _vp, _c_float, _c_float, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_norm_quant_nvfp4": (_c_int, [_vp, _vp, _c_float, _c_float, _vp, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_norm_quant_nvfp4_rank_block": (_c_int, [_vp, _c_int, _vp, _c_float, _c_float, _vp, _c_int, _c_int,
                                                  _vp, _vp, _vp]),
@@ -252,14 +252,15 @@ def route_dispatch_quant(hidden: Optional[torch.Tensor], W: Optional[torch.Tenso
                          logits=None, topk_ids=None, topk_w=None, counts=None, offsets=None, perm=None, dest=None,
                          packed=None, scales=None, workspace: Optional[torch.Tensor] = None):
     """moe_route_dispatch_quant: route_dispatch() and norm_quant_nvfp4() of x
-    in one call. x [T,H] bf16 with hidden's T and H. Returns (logits,
-    topk_ids, topk_w, counts, offsets, perm, dest, packed, scales)."""
+    in one call. x [T,Hq] bf16 with hidden's T and a width of its own.
+    Returns (logits, topk_ids, topk_w, counts, offsets, perm, dest, packed,
+    scales)."""
     dev = bias.device
     T, H, E, dtype, logits, topk_ids, topk_w = _route_io(hidden, W, bias, token_mask, k, logits, topk_ids, topk_w)
     counts, offsets, perm, dest = _dispatch_io(dev, T, k, E, counts, offsets, perm, dest)
     _need(x, "x", _BF16, None, dev)
-    if x.dim() != 2 or x.shape[0] != T or (hidden is not None and x.shape[1] != H):
-        raise ValueError("x must be [T,H] with hidden's T and H")
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T,Hq] with hidden's T")
     Hx = x.shape[1]
     _need(norm_w, "norm_w", (torch.float32,), (Hx,), dev)
     _need(global_scale, "global_scale", (torch.float32,), (1,), dev)
@@ -270,9 +271,9 @@ def route_dispatch_quant(hidden: Optional[torch.Tensor], W: Optional[torch.Tenso
     workspace, ws_len = _workspace(workspace, route_dispatch_workspace_bytes(T, H, E, k, dtype, hidden is None),
                                    dev)
     _check("moe_route_dispatch_quant", lib().moe_route_dispatch_quant(
-        _ptr(hidden), dtype, _ptr(W), _ptr(bias), _ptr(token_mask), float(scale), T, Hx, E, k,
+        _ptr(hidden), dtype, _ptr(W), _ptr(bias), _ptr(token_mask), float(scale), T, H, E, k,
         _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(dest),
-        _ptr(x), _ptr(norm_w), float(gain_center), float(eps), _ptr(global_scale), _ptr(packed), _ptr(scales),
+        _ptr(x), Hx, _ptr(norm_w), float(gain_center), float(eps), _ptr(global_scale), _ptr(packed), _ptr(scales),
         _ptr(workspace), ws_len, _stream(dev)))
     return logits, topk_ids, topk_w, counts, offsets, perm, dest, packed, scales
 

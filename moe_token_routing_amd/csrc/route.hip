@@ -738,11 +738,11 @@ namespace moe {
 namespace {
 
 // The steps of moe_route_dispatch and moe_route_dispatch_quant (x == nullptr:
-// no norm + quant) after their own argument checks.
+// no norm + quant; x is [T, Hq]) after their own argument checks.
 int route_dispatch_run(const void* hidden, int hidden_dtype, const float* W, const float* bias,
                        const uint8_t* token_mask, float scale, int T, int H, int E, int k, float* logits,
                        int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
-                       int32_t* dest, const uint16_t* x, const float* norm_w, float gain_center, float eps,
+                       int32_t* dest, const uint16_t* x, int Hq, const float* norm_w, float gain_center, float eps,
                        const float* global_scale, uint8_t* packed, uint8_t* scales, void* workspace,
                        size_t workspace_bytes, void* stream) {
     if (T == 0) return run_dispatch_empty(counts, offsets, E, stream);
@@ -760,7 +760,7 @@ int route_dispatch_run(const void* hidden, int hidden_dtype, const float* W, con
     if (rc) return rc;
     if (!x) return run_place(topk_ids, n, E, counts, offsets, perm, dest, hist, stream);
     return run_place_norm_quant(topk_ids, n, E, counts, offsets, perm, dest, hist, x, norm_w, gain_center, eps,
-                                global_scale, T, H, packed, scales, stream);
+                                global_scale, T, Hq, packed, scales, stream);
 }
 
 }  // namespace
@@ -777,7 +777,7 @@ extern "C" int moe_route_dispatch(const void* hidden, int hidden_dtype, const fl
     rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
     if (rc) return rc;
     return route_dispatch_run(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
-                              counts, offsets, perm, dest, nullptr, nullptr, 0.f, 0.f, nullptr, nullptr, nullptr,
+                              counts, offsets, perm, dest, nullptr, 0, nullptr, 0.f, 0.f, nullptr, nullptr, nullptr,
                               workspace, workspace_bytes, stream);
 }
 
@@ -785,7 +785,7 @@ extern "C" int moe_route_dispatch_quant(const void* hidden, int hidden_dtype, co
                                         const uint8_t* token_mask, float scale, int T, int H, int E, int k,
                                         float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
                                         int32_t* offsets, int32_t* perm, int32_t* dest, const uint16_t* x,
-                                        const float* norm_w, float gain_center, float eps,
+                                        int Hq, const float* norm_w, float gain_center, float eps,
                                         const float* global_scale, uint8_t* packed, uint8_t* scales,
                                         void* workspace, size_t workspace_bytes, void* stream) {
     using namespace moe;
@@ -793,9 +793,9 @@ extern "C" int moe_route_dispatch_quant(const void* hidden, int hidden_dtype, co
     if (rc) return rc;
     rc = check_dispatch(topk_ids, T, k, E, counts, offsets, perm, dest);
     if (rc) return rc;
-    rc = check_norm_quant(x, norm_w, gain_center, eps, global_scale, T, H, packed, scales);
+    rc = check_norm_quant(x, norm_w, gain_center, eps, global_scale, T, Hq, packed, scales);
     if (rc) return rc;
     return route_dispatch_run(hidden, hidden_dtype, W, bias, token_mask, scale, T, H, E, k, logits, topk_ids, topk_w,
-                              counts, offsets, perm, dest, x, norm_w, gain_center, eps, global_scale, packed, scales,
+                              counts, offsets, perm, dest, x, Hq, norm_w, gain_center, eps, global_scale, packed, scales,
                               workspace, workspace_bytes, stream);
 }

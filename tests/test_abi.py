@@ -148,13 +148,14 @@ def test_route_dispatch_rejects_before_launch(lib):
 def test_route_dispatch_quant_rejects_before_launch(lib):
     f = lib.moe_route_dispatch_quant
 
-    def call(hidden=FAKE, W=FAKE, T=4, H=64, E=16, k=4, counts=FAKE, x=FAKE, nw=FAKE, gc=1.0, eps=1e-6, gs=FAKE,
-             packed=FAKE, scales=FAKE, ws=FAKE, wsb=1 << 30):
+    def call(hidden=FAKE, W=FAKE, T=4, H=64, E=16, k=4, counts=FAKE, x=FAKE, Hq=32, nw=FAKE, gc=1.0, eps=1e-6,
+             gs=FAKE, packed=FAKE, scales=FAKE, ws=FAKE, wsb=1 << 30):
         return f(hidden, 1, W, FAKE, FAKE, 1.0, T, H, E, k, FAKE, FAKE, FAKE, counts, FAKE, FAKE, FAKE,
-                 x, nw, gc, eps, gs, packed, scales, ws, wsb, None)
+                 x, Hq, nw, gc, eps, gs, packed, scales, ws, wsb, None)
 
     assert call(k=17) == -2 and call(H=24) == -2 and call(counts=None) == -1     # route, dispatch
     assert call(x=None) == -1 and call(gs=None) == -1 and call(packed=None) == -1  # norm + quant
+    assert call(Hq=24) == -2 and call(Hq=0) == -2 and call(Hq=(1 << 20)) == -2    # the expert input's width
     assert call(eps=-1.0) == -5 and call(gc=float("nan")) == -5
     assert call(x=V((1 << 20) + 2)) == -7
     assert call(ws=None) == -4

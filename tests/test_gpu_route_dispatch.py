@@ -192,16 +192,23 @@ def _quant_inputs(w, T, H):
 # prefill (8192 and 3000 tokens) and large E (H 4096) take the one-launch
 # path (the latter after the separate column scan); decode (too few tokens),
 # wide top-22 (H 1024) and tiny (one tile, H 256) run the two steps in turn.
-@pytest.mark.parametrize("name,T", [("prefill", None), ("prefill", 3000), ("large_e", None), ("decode", None),
-                                    ("wide_k", 2000), ("tiny", None)])
-def test_route_dispatch_quant_matches_separate_calls(name, T):
+# The expert input may be narrower or wider than the router's (Hq): 4096 (a
+# pooled stream half the router's width), 12288 and 16384 (three and four
+# 16-element blocks per thread in the one-launch path), 1024 and 2064 (rows
+# that do not fill a 256-thread block: the two steps in turn).
+@pytest.mark.parametrize("name,T,Hq", [("prefill", None, None), ("prefill", 3000, None), ("large_e", None, None),
+                                       ("decode", None, None), ("wide_k", 2000, None), ("tiny", None, None),
+                                       ("prefill", 3000, 4096), ("prefill", 3000, 12288), ("prefill", 3000, 16384),
+                                       ("prefill", 3000, 1024), ("large_e", None, 2064), ("tiny", None, 8192)])
+def test_route_dispatch_quant_matches_separate_calls(name, T, Hq):
     require_gpu()
     w = wl.WORKLOADS[name]
     T = w.T if T is None else T
-    note("route_dispatch_quant %s T=%d" % (name, T))
+    note("route_dispatch_quant %s T=%d Hq=%s" % (name, T, Hq))
     hidden = wl.hidden(w, T)
     H = hidden.shape[1]
-    x, nw = _quant_inputs(w, T, H)
+    Hq = H if Hq is None else Hq
+    x, nw = _quant_inputs(w, T, Hq)
     h_d, W_d, b_d, m_d = dev(hidden), dev(wl.router_weight(w)), dev(wl.bias(w)), dev(wl.token_mask(w, T))
     x_d, nw_d = dev(x), dev(nw)
     gs = torch.tensor([345.44577], dtype=torch.float32, device=DEV)
@@ -209,8 +216,9 @@ def test_route_dispatch_quant_matches_separate_calls(name, T):
     sep = [host(t) for t in m.route_dispatch(h_d, W_d, b_d, m_d, w.k)]
     sep += [host(t) for t in m.norm_quant_nvfp4(x_d, nw_d, 1.0, 1e-6, gs)]
     torch.cuda.synchronize()
+    assert fus[-2].shape == (T, Hq // 2) and fus[-1].shape == (T, Hq // 16)
     for n_, a, b in zip(NQ_NAMES, fus, sep):
-        np.testing.assert_array_equal(a, b, err_msg="%s T=%d: %s" % (name, T, n_))
+        np.testing.assert_array_equal(a, b, err_msg="%s T=%d Hq=%d: %s" % (name, T, Hq, n_))
 
 
 def test_route_dispatch_quant_graph_replay():
