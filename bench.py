@@ -42,9 +42,11 @@ Alongside the throughput the line carries:
   stages        per-call mean duration (HIP events on the launch stream, from
                 a serial eager pass; route_dispatch from a fused pass) and
                 algorithmic bytes / achieved GB/s
-  schedules     ms per step of every schedule, and of the serial one with the
-                256 MB last-level cache flushed before each step (cold); the
-                p10 / median / p90 of single serial steps (HIP events)
+  schedules     ms per step of every schedule, and of the serial and the
+                headline one with the 256 MB last-level cache flushed before
+                each step (cold: by a 512 MiB write, and by a 512 MiB read,
+                which leaves no dirty lines to write back); the p10 / median
+                / p90 of single serial steps (HIP events)
   roofline      the dominant kernel (the combine) against MI355X's 8 TB/s:
                 algorithmic bytes per launch / mean launch duration; `traffic`
                 is the HBM bytes per launch from the committed rocprofv3
@@ -539,18 +541,31 @@ def main():
     prepare_fused_graph_ms = (ms_per_step if args.graph and args.schedule == "prepare-fused"
                               else graph_ms(step_prepare_fused))
 
-    # cold: flush the 256 MB last-level cache (a 512 MiB write) before each step
-    cold_ms = None
+    # cold: the 256 MB last-level cache flushed before each step, outside its
+    # events, by a 512 MiB write (which leaves up to the cache's size of dirty
+    # lines, whose write-back the step then pays) or by a 512 MiB read (which
+    # only evicts)
+    cold_ms = cold_read_ms = head_cold_ms = head_cold_read_ms = None
     if args.cold_steps > 0:
         flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
-        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.cold_steps)]
-        for a, b in ce:
-            flush.fill_(1)
-            a.record(stream)
-            step_serial()
-            b.record(stream)
-        torch.cuda.synchronize()
-        cold_ms = float(np.mean([a.elapsed_time(b) for a, b in ce]))
+        flush.fill_(1)
+
+        def cold(step_fn, by_read):
+            ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.cold_steps)]
+            for a, b in ce:
+                if by_read:
+                    flush.max()
+                else:
+                    flush.fill_(1)
+                a.record(stream)
+                step_fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in ce]))
+
+        cold_ms, cold_read_ms = cold(step_serial, False), cold(step_serial, True)
+        head_cold_ms, head_cold_read_ms = cold(head_step, False), cold(head_step, True)
         del flush
 
     # norm + quant reading the rank-block layout of 8 column shards
@@ -664,6 +679,9 @@ def main():
                       "overlap_graph_ms": round(overlap_graph_ms, 4),
                       "serial_graph_ms": round(serial_graph_ms, 4),
                       "serial_cold_ms": None if cold_ms is None else round(cold_ms, 4),
+                      "serial_cold_read_flush_ms": None if cold_read_ms is None else round(cold_read_ms, 4),
+                      "headline_cold_ms": None if head_cold_ms is None else round(head_cold_ms, 4),
+                      "headline_cold_read_flush_ms": None if head_cold_read_ms is None else round(head_cold_read_ms, 4),
                       "serial_steps": serial_spread},
         "device_copy_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "hbm_frac_of_device_copy": None if copy_gbs is None else round(hbm_gbs / copy_gbs, 4),
