@@ -331,17 +331,26 @@ __device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, 
 // Experts e = EPL*lane + i (i < EPL) live in lane e / EPL, so each lane reads
 // its logits (or split partials) as one contiguous run. BATCH split partials
 // are loaded before any of them is added: 8 keep the registers of many waves
-// per SIMD (large batches split K 8 ways); 32 cut the dependent rounds of
-// loads when a small batch split K many ways (64 at 128 tokens).
-template <int EPL, int BATCH, bool THRESHOLD, bool FULL>
+// per SIMD (large batches split K 8 ways).
+// WPT waves per token: with WPT = 4 (small batches, whose projection splits
+// K many ways: 64 at 128 tokens) a block is one token and its four waves
+// each sum a contiguous quarter of the splits, so a token's partials are
+// read by one CU's four SIMDs at once (and the batch by four times as many
+// CUs); the quarter sums meet in LDS, added in order to the first, and the
+// first wave goes on alone.
+template <int EPL, int BATCH, bool THRESHOLD, bool FULL, int WPT = 1>
 __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
     const float* __restrict__ partials, int nsplit, float scale, int logits_in,
     const float* __restrict__ bias, const uint8_t* __restrict__ token_mask, int T, int E, int k,
     float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ hist, int hist_tile) {
+    static_assert(WPT == 1 || WPT == kSelectWaves, "one token per wave or per block");
     const int lane = __lane_id();
-    const int t = blockIdx.x * kSelectWaves + threadIdx.x / kWave;
-    if (t >= T) return;   // whole wave leaves together
+    const int wq = WPT == 1 ? 0 : static_cast<int>(threadIdx.x) / kWave;   // quarter of the splits
+    const int t = WPT == 1 ? blockIdx.x * kSelectWaves + static_cast<int>(threadIdx.x) / kWave
+                           : static_cast<int>(blockIdx.x);
+    if (t >= T) return;   // whole wave (WPT = 4: whole block) leaves together
+    if (WPT > 1 && logits_in && wq > 0) return;   // (not launched so: nothing to sum)
     const size_t plane = static_cast<size_t>(T) * E;
     const bool valid = token_mask[t] != 0;
     const int e0 = EPL * lane;
@@ -352,25 +361,31 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
 
     float lg[EPL], bs[EPL];
     // the lane's biases, loaded with its logits (before any store)
-    if (n > 0) {
+    if (n > 0 && wq == 0) {
         load_run<EPL, FULL>(bias + e0, vec, n, bs);
     } else {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) bs[i] = 0.f;
     }
+    // this wave's splits [s0, s1): all of them, or (WPT = 4) a contiguous
+    // quarter, every quarter nonempty (nsplit > 9 when WPT = 4)
+    const int per = (nsplit + WPT - 1) / WPT;
+    const int s0 = wq * per, s1 = min(nsplit, s0 + per);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) lg[i] = 0.f;
     if (n > 0) {
         if (logits_in) {
             load_run<EPL, FULL>(logits + row, vec, n, lg);
         } else {
-            load_run<EPL, FULL>(partials + row, vec, n, lg);
+            load_run<EPL, FULL>(partials + s0 * plane + row, vec, n, lg);
             // a batch of splits is loaded before any is added (the loads
             // overlap); the sum still runs over the splits in order
 #pragma unroll 1
-            for (int p0 = 1; p0 < nsplit; p0 += BATCH) {
+            for (int p0 = s0 + 1; p0 < s1; p0 += BATCH) {
                 float q[BATCH][EPL];
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u) {
-                    if (p0 + u < nsplit) {
+                    if (p0 + u < s1) {
                         load_run<EPL, FULL>(partials + (p0 + u) * plane + row, vec, n, q[u]);
                     } else {
 #pragma unroll
@@ -379,16 +394,35 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
                 }
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u)
-                    if (p0 + u < nsplit) {
+                    if (p0 + u < s1) {
 #pragma unroll
                         for (int i = 0; i < EPL; ++i) lg[i] += q[u][i];
                     }
             }
+        }
+    }
+    if constexpr (WPT > 1) {
+        if (!logits_in) {
+            // the quarters meet: waves 1..3 hand their sums to wave 0, which
+            // adds them in order (uniform control flow around the barrier)
+            __shared__ float quarter[WPT - 1][EPL][kWave];
+            if (wq > 0) {
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                lg[i] *= scale;
-                if (i < n) logits[row + i] = lg[i];
+                for (int i = 0; i < EPL; ++i) quarter[wq - 1][i][lane] = lg[i];
             }
+            __syncthreads();
+            if (wq > 0) return;
+#pragma unroll
+            for (int w = 0; w < WPT - 1; ++w)
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) lg[i] += quarter[w][i][lane];
+        }
+    }
+    if (n > 0 && !logits_in) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            lg[i] *= scale;
+            if (i < n) logits[row + i] = lg[i];
         }
     }
     int32_t* ids = topk_ids + static_cast<size_t>(t) * k;
@@ -690,14 +724,14 @@ __global__ __launch_bounds__(kSelectBlock) void select_lds_kernel(
     count_pick(hist, hist_tile, E, t, k, lane, my_id);
 }
 
-template <int EPL, int BATCH>
+template <int EPL, int BATCH, int WPT = 1>
 int launch_select_reg2(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
                        const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
                        int32_t* hist, int hist_tile, void* stream) {
-    const dim3 grid(ceil_div(T, kSelectWaves));
+    const dim3 grid(ceil_div(T, kSelectWaves / WPT));
 #define MOE_SELECT(THR, FULL)                                                                                 \
-    return launch(select_reg_kernel<EPL, BATCH, THR, FULL>, grid, dim3(kSelectBlock), 0, stream, partials, nsplit, \
-                  scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile)
+    return launch(select_reg_kernel<EPL, BATCH, THR, FULL, WPT>, grid, dim3(kSelectBlock), 0, stream, partials,  \
+                  nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile)
     const bool full = E == EPL * kWave;   // then E % 4 == 0 and every row is 16-byte aligned
     if (k >= kThresholdPicks) {
         if (full) MOE_SELECT(true, true);
@@ -712,9 +746,12 @@ template <int EPL>
 int launch_select_reg(const float* partials, int nsplit, float scale, int logits_in, const float* bias,
                       const uint8_t* mask, int T, int E, int k, float* logits, int32_t* ids, float* w,
                       int32_t* hist, int hist_tile, void* stream) {
-    if (nsplit > 2 * kSplitBatch)
-        return launch_select_reg2<EPL, 4 * kSplitBatch>(partials, nsplit, scale, logits_in, bias, mask, T, E, k,
-                                                        logits, ids, w, hist, hist_tile, stream);
+    // many splits (a small batch): four waves per token, each summing a
+    // quarter of the splits, up to 16 loads in flight per lane (8 with 8
+    // experts a lane, for its registers)
+    if (nsplit > 2 * kSplitBatch && !logits_in)
+        return launch_select_reg2<EPL, (EPL <= 4 ? 2 : 1) * kSplitBatch, kSelectWaves>(
+            partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits, ids, w, hist, hist_tile, stream);
     return launch_select_reg2<EPL, kSplitBatch>(partials, nsplit, scale, logits_in, bias, mask, T, E, k, logits,
                                                 ids, w, hist, hist_tile, stream);
 }

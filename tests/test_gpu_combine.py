@@ -133,3 +133,30 @@ def test_combine_empty_and_zero_rows():
                     torch.empty((0, 2), dtype=torch.float32, device=DEV),
                     torch.ones(64, dtype=torch.float32, device=DEV), 0.0, 1e-6)
     assert out.shape == (0, 64)
+
+
+@pytest.mark.parametrize("T,k,H", [(1, 1, 8192), (5, 32, 8192), (3, 7, 16384), (256, 8, 8192), (300, 8, 8192)])
+def test_combine_one_token_per_cu(T, k, H):
+    """Batches of no more tokens than CUs at widths of whole 1024-vector
+    multiples take one 1024-thread block per token (300 tokens: the
+    256-thread blocks, beside it): k off the four-row groups, a whole token
+    invalid, out-of-range slots, and power-of-two rows exact with eps = 0."""
+    g = np.random.default_rng(T * k + H)
+    R = T * k + 5
+    eo = wl.f32_to_bf16_bits((g.standard_normal((R, H)) * 3).astype(np.float32))
+    slots = g.permutation(R)[:T * k].astype(np.int32).reshape(T, k)
+    slots[0, 0] = -1
+    if T > 2:
+        slots[1, :] = -1
+        slots[2, -1] = R + 3
+    tw = g.uniform(0, 1, (T, k)).astype(np.float32)
+    gain = g.uniform(-1.5, 1.5, H).astype(np.float32)
+    _run_and_check(eo, slots, tw, gain, 0.5, 1e-6, what="one token per CU T=%d k=%d H=%d" % (T, k, H))
+    rows = g.choice([-1.0, 1.0], (R, H)) * 2.0 ** g.integers(-3, 3, (R, 1))
+    eo = wl.f32_to_bf16_bits(rows.astype(np.float32))
+    gain = O.round_bf16(g.uniform(0.5, 1.5, H)).astype(np.float32)
+    tw = (2.0 ** g.integers(-3, 1, (T, k))).astype(np.float32)
+    note("combine power-of-two exact T=%d k=%d H=%d" % (T, k, H))
+    out = m.combine(dev(eo), dev(slots), dev(tw), dev(gain), 0.0, 0.0)
+    ref, _ = O.combine(eo, slots, tw, gain, 0.0, 0.0)
+    np.testing.assert_array_equal(host(out), ref)
