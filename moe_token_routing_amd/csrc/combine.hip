@@ -14,8 +14,10 @@
 // threads), each normalised row is rounded to BF16 two elements at a time
 // (v_cvt_pk_bf16_f32) and the weighted rows accumulate in FP32 registers in
 // slot order (one FMA per element). That is about six VALU operations per
-// element, so the kernel stays under the HBM time. The per-element gain stays
-// in registers across the tokens a block visits (grid-stride loop).
+// element, so the kernel stays under the HBM time. The per-element gain is
+// staged in LDS once per block and read there for every token the block
+// visits (grid-stride loop). With no more tokens than CUs, one 1024-thread
+// block serves each token.
 #include <cmath>
 
 #include "launch.hpp"

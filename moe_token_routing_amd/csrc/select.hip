@@ -8,7 +8,9 @@
 // invalid token produces no routing entry; the aux-loss-free gate uses the
 // bias only to select).
 //
-// Design (gfx950): one wave per token. For E <= 512 the experts of a lane are
+// Design (gfx950): one wave per token (for small batches, whose projection
+// splits K many ways, four waves sum a token's partials and the first goes
+// on alone). For E <= 512 the experts of a lane are
 // consecutive (lane e / EPL), so logits and split partials arrive as 16-byte
 // vector loads; beyond that expert e lives in lane e % 64 of an LDS copy. The
 // sigmoid is evaluated in FP64 and rounded once to FP32 (a correctly rounded
