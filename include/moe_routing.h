@@ -198,9 +198,9 @@ int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, con
  * TensorRT-LLM PR #21356, "Where they plug in": the expert input's norm and
  * quantisation run beside the routing (on an auxiliary stream there). Here
  * the dispatch's place step and the norm + quant share one launch, blocks of
- * each side by side, when x's rows fill whole blocks of the staged norm +
- * quant (Hq / 16 = 256, 512, 768 or 1024) and there are more tokens than its
- * blocks; otherwise they run one after the other. Same outputs either way:
+ * each side by side, when x's rows fill a wave or whole 256-thread blocks
+ * (Hq / 16 = 64, 256, 512, 768 or 1024); otherwise they run one after the
+ * other. Same outputs either way:
  * every output is bit-identical to moe_route_dispatch followed by
  * moe_norm_quant_nvfp4.
  *

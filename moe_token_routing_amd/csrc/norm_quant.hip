@@ -178,9 +178,9 @@ __device__ __forceinline__ void load_gains(const float* norm_w, int b, float gai
 // thread (H / 16 = BPT TPT), so the token is the same for the whole wave
 // and the per-block bounds checks disappear.
 template <int BPT, int TPT>
-__global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
-    const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
-    const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
+__device__ __forceinline__ void norm_quant_body(
+    int blk, int nblocks, const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center,
+    float eps, const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
     uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     __shared__ float red[kRowBlock / kWave];
     __shared__ float outs_of[256];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
     }
     const bool gok = gains_finite<BPT>(gain);
 
-    for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
+    for (int t0 = blk * tokens_per_block; t0 < T; t0 += nblocks * tokens_per_block) {
         const int t = t0 + sub;
         const bool tok_ok = t < T;
         uint32_t xw[BPT][8];   // block i: 16 BF16 values as 8 packed pairs
@@ -249,6 +249,15 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
             }
         }
     }
+}
+
+template <int BPT, int TPT>
+__global__ __launch_bounds__(kRowBlock) void norm_quant_kernel(
+    const u32x4* __restrict__ x, const float* __restrict__ norm_w, float gain_center, float eps,
+    const float* __restrict__ global_scale, int T, int H, int shard8, int tpt,
+    uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
+    norm_quant_body<BPT, TPT>(blockIdx.x, gridDim.x, x, norm_w, gain_center, eps, global_scale, T, H, shard8, tpt,
+                              packed, scales);
 }
 
 // 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
@@ -404,7 +413,10 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
 // bandwidth-bound norm + quant instead of before it, with no second stream
 // to fork and join (TensorRT-LLM PR #21356, "Where they plug in": the
 // expert input prepared beside the routing).
-template <int MODE, int BPT>
+// ONE_TPT = 0: the staged norm + quant (one token per block, each block
+// visiting several); ONE_TPT = kWave or kRowBlock: the one-pass form, for
+// batches with fewer tokens than the launch has blocks (small batches).
+template <int MODE, int BPT, int ONE_TPT = 0>
 __global__ __launch_bounds__(kRowBlock) void place_norm_quant_kernel(
     int n_place, const int32_t* __restrict__ ids, int n, int E, int tile, int tiles,
     const int32_t* __restrict__ tile_hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -415,9 +427,12 @@ __global__ __launch_bounds__(kRowBlock) void place_norm_quant_kernel(
     extern __shared__ __attribute__((aligned(16))) int32_t place_lds[];
     if (static_cast<int>(blockIdx.x) < n_place)
         place_body<MODE>(blockIdx.x, place_lds, ids, n, E, tile, tiles, tile_hist, counts, offsets, perm, dest);
-    else
+    else if constexpr (ONE_TPT == 0)
         norm_quant_staged_body<BPT, kRowBlock>(blockIdx.x - n_place, gridDim.x - n_place, x, norm_w, gain_center,
                                                eps, global_scale, T, H, H / 8, packed, scales);
+    else
+        norm_quant_body<BPT, ONE_TPT>(blockIdx.x - n_place, gridDim.x - n_place, x, norm_w, gain_center, eps,
+                                      global_scale, T, H, H / 8, ONE_TPT, packed, scales);
 }
 
 struct BlockGeom {
@@ -474,16 +489,28 @@ int check_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, 
 
 namespace {
 
-template <int MODE, int BPT>
+template <int MODE, int BPT, int ONE_TPT = 0>
 int launch_place_norm_quant(int grid, int n_place, size_t lds, const int32_t* topk_ids, int n, int E, int tile,
                             int tiles, int32_t* tile_counts, int32_t* counts, int32_t* offsets, int32_t* perm,
                             int32_t* dest, const uint16_t* x, const float* norm_w, float gain_center, float eps,
                             const float* global_scale, int T, int H, uint8_t* packed, uint8_t* scales,
                             void* stream) {
-    return launch(place_norm_quant_kernel<MODE, BPT>, dim3(grid), dim3(kRowBlock), lds, stream, n_place, topk_ids,
+    return launch(place_norm_quant_kernel<MODE, BPT, ONE_TPT>, dim3(grid), dim3(kRowBlock), lds, stream, n_place, topk_ids,
                   n, E, tile, tiles, static_cast<const int32_t*>(tile_counts), counts, offsets, perm, dest,
                   reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
                   reinterpret_cast<uint2*>(packed), scales);
+}
+
+// Blocks of place_norm_quant_kernel<MODE, bpt, one_tpt> resident per CU.
+template <int MODE>
+int resident_place_norm_quant_one(int bpt, int one_tpt, size_t lds) {
+    if (one_tpt == kWave) return resident_blocks(place_norm_quant_kernel<MODE, 1, kWave>, kRowBlock, lds);
+    switch (bpt) {
+        case 1: return resident_blocks(place_norm_quant_kernel<MODE, 1, kRowBlock>, kRowBlock, lds);
+        case 2: return resident_blocks(place_norm_quant_kernel<MODE, 2, kRowBlock>, kRowBlock, lds);
+        case 3: return resident_blocks(place_norm_quant_kernel<MODE, 3, kRowBlock>, kRowBlock, lds);
+        default: return resident_blocks(place_norm_quant_kernel<MODE, 4, kRowBlock>, kRowBlock, lds);
+    }
 }
 
 template <int MODE>
@@ -532,6 +559,42 @@ int run_place_norm_quant(const int32_t* topk_ids, long long n, int E, int32_t* c
             MOE_PNQ(kPlaceScanned, 1) MOE_PNQ(kPlaceScanned, 2) MOE_PNQ(kPlaceScanned, 3) MOE_PNQ(kPlaceScanned, 4)
 #undef MOE_PNQ
         }
+    }
+    // Otherwise (too few tokens for the staged form to pay, or rows of 64
+    // blocks, one token per wave) the one-pass norm + quant shares the
+    // launch, over as many blocks as its tokens need up to the GPU's resident
+    // capacity; blocks beyond what is resident wait their turn, as nothing
+    // waits on another block.
+    const int one_tpt =
+        (geo.tpt == kRowBlock || (geo.tpt == kWave && geo.bpt == 1)) && H / 16 == geo.bpt * geo.tpt && geo.bpt <= 4
+            ? geo.tpt : 0;
+    if (one_tpt && n > 0 && T > 0) {
+        const int mode = place_mode(n, E);
+        const DispatchTiles d = dispatch_tiles(n);
+        const int n_place = mode == kPlaceSingle ? 1 : d.tiles;
+        const size_t lds = place_lds_bytes(mode, E);
+        const int per_cu = mode == kPlaceSingle ? resident_place_norm_quant_one<kPlaceSingle>(geo.bpt, one_tpt, lds)
+                           : mode == kPlaceFused ? resident_place_norm_quant_one<kPlaceFused>(geo.bpt, one_tpt, lds)
+                                                 : resident_place_norm_quant_one<kPlaceScanned>(geo.bpt, one_tpt, lds);
+        const int needed = ceil_div(T, kRowBlock / one_tpt);
+        const int room = device_cu_count() * per_cu - n_place;
+        const int n_nq = min(needed, max(room, device_cu_count()));
+        if (mode == kPlaceScanned) {
+            const int rc = run_scan(tile_counts, n, E, counts, stream);
+            if (rc) return rc;
+        }
+#define MOE_PNQ1(M, B, TP)                                                                                      \
+    if (mode == M && geo.bpt == B && one_tpt == TP)                                                             \
+        return launch_place_norm_quant<M, B, TP>(n_place + n_nq, n_place, lds, topk_ids, static_cast<int>(n), E,  \
+                                                 d.tile, d.tiles, tile_counts, counts, offsets, perm, dest, x,    \
+                                                 norm_w, gain_center, eps, global_scale, T, H, packed, scales,   \
+                                                 stream);
+#define MOE_PNQ1_MODE(M) \
+    MOE_PNQ1(M, 1, kWave) MOE_PNQ1(M, 1, kRowBlock) MOE_PNQ1(M, 2, kRowBlock) MOE_PNQ1(M, 3, kRowBlock) \
+    MOE_PNQ1(M, 4, kRowBlock)
+        MOE_PNQ1_MODE(kPlaceSingle) MOE_PNQ1_MODE(kPlaceFused) MOE_PNQ1_MODE(kPlaceScanned)
+#undef MOE_PNQ1_MODE
+#undef MOE_PNQ1
     }
     int rc = n > 0 ? run_place(topk_ids, n, E, counts, offsets, perm, dest, tile_counts, stream)
                    : run_dispatch_empty(counts, offsets, E, stream);
