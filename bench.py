@@ -53,7 +53,8 @@ Alongside the throughput the line carries:
                 counter summary, when that was taken on the current kernel
                 source (null otherwise)
   expert_fc1    the expert FC1 (moe_expert_fc1_nvfp4) at the FC1 workload of
-                the act-fusion GEMM page, against the FP16 MFMA peak
+                the act-fusion GEMM page, against the FP16 MFMA peak (32768
+                tokens; 8192 and 65536 tokens, the page's other two, beside)
   expert_fc1_swiglu  the SwiGLU form (moe_expert_fc1_swiglu_nvfp4) over the
                 same 2688 weight rows as gate and up halves
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
@@ -201,14 +202,14 @@ def cpu_baseline(w, sample_tokens: int, workers: int):
                       % (S, w.name, dt, how)}
 
 
-def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10, swiglu: bool = False):
+def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10, swiglu: bool = False, tokens=None):
     """The expert FC1 on the dispatched NVFP4 input at the FC1 workload the
     act-fusion GEMM page times (K 1024, N 2688, 512 experts, top-22, 32768
-    tokens): synthetic NVFP4 bytes, the path's own dispatch of synthetic
-    top-22 ids, HIP events around each call. swiglu: the same 2688 weight
-    rows as gate and up halves (1344 output columns)."""
+    tokens, or `tokens`): synthetic NVFP4 bytes, the path's own dispatch of
+    synthetic top-22 ids, HIP events around each call. swiglu: the same 2688
+    weight rows as gate and up halves (1344 output columns)."""
     w = wl.WORKLOADS["wide_k"]
-    T, k, E, K = w.T, w.k, w.E, w.H
+    T, k, E, K = w.T if tokens is None else tokens, w.k, w.E, w.H
     N = wl.FC1_SWIGLU_N["wide_k"] if swiglu else wl.FC1_N["wide_k"]
     rows = 2 * N if swiglu else N
     xp, xs = wl.fc1_activations(w, T, K)
@@ -240,7 +241,7 @@ def time_expert_fc1(m, wl, torch, dev, stream, reps: int = 10, swiglu: bool = Fa
     flop = 2.0 * T * k * rows * K
     tf = flop / (ms * 1e-3) / 1e12
     what = ("SwiGLU, 1344 output columns over 2688 gate and up rows" if swiglu else "Relu2, N 2688")
-    return {"workload": "K 1024, %s, 512 experts, top-22, 32768 tokens (720896 routed rows)" % what,
+    return {"workload": "K 1024, %s, 512 experts, top-22, %d tokens (%d routed rows)" % (what, T, T * k),
             "ms": round(ms, 3), "TFLOPs": round(tf, 1), "unit_peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
             "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
             "bytes_in": int(T * K * 9 // 16 + E * rows * K * 9 // 16), "bytes_out": int(T * k * N * 9 // 16)}
@@ -593,6 +594,12 @@ def main():
     if args.fc1:
         fc1 = time_expert_fc1(m, wl, torch, dev, stream)
         fc1_swiglu = time_expert_fc1(m, wl, torch, dev, stream, swiglu=True)
+        # the other token counts the act-fusion GEMM page times the FC1 at
+        fc1["other_token_counts"] = {}
+        for tok in (8192, 65536):
+            r = time_expert_fc1(m, wl, torch, dev, stream, tokens=tok)
+            fc1["other_token_counts"][str(tok)] = {k_: r[k_] for k_ in ("ms", "TFLOPs", "frac_of_fp16_mfma_peak")}
+            torch.cuda.empty_cache()
 
     names = ["route", "dispatch", "norm_quant", "combine"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
