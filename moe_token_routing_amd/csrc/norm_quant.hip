@@ -449,6 +449,12 @@ inline BlockGeom block_geom(int H) {
     return g;
 }
 
+// Blocks per CU of the staged norm + quant (fewer than fit: each then visits
+// more tokens, and fewer rows are in flight at once). At 8192 tokens of 8192
+// after a read flush: 36.3 us at the 5 that fit, 36.3 at 4, 35.2-35.6 at 3,
+// 34.6 at 2.
+constexpr int kStagedPerCu = 3;
+
 template <int BPT, int TPT>
 int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, float eps,
                       const float* global_scale, int T, int H, int shard, const BlockGeom& geo,
@@ -459,8 +465,8 @@ int launch_norm_quant(const uint16_t* x, const float* norm_w, float gain_center,
     const int cap = device_cu_count() * resident_blocks(norm_quant_kernel<BPT, TPT>, kRowBlock, 0);
     if constexpr (TPT != 0) {
         // blocks that visit several tokens copy each next row in ahead
-        const int cap_staged =
-            device_cu_count() * resident_blocks(norm_quant_staged_kernel<BPT, TPT>, kRowBlock, 0);
+        const int fit = resident_blocks(norm_quant_staged_kernel<BPT, TPT>, kRowBlock, 0);
+        const int cap_staged = device_cu_count() * (fit < kStagedPerCu ? fit : kStagedPerCu);
         if (needed > cap_staged)
             return launch(norm_quant_staged_kernel<BPT, TPT>, dim3(cap_staged), dim3(kRowBlock), 0, stream,
                           reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
@@ -542,7 +548,8 @@ int run_place_norm_quant(const int32_t* topk_ids, long long n, int E, int32_t* c
         const int per_cu = mode == kPlaceSingle ? resident_place_norm_quant<kPlaceSingle>(geo.bpt, lds)
                            : mode == kPlaceFused ? resident_place_norm_quant<kPlaceFused>(geo.bpt, lds)
                                                  : resident_place_norm_quant<kPlaceScanned>(geo.bpt, lds);
-        const int grid = device_cu_count() * per_cu;   // every block resident at once
+        // every block resident at once
+        const int grid = device_cu_count() * (per_cu < kStagedPerCu ? per_cu : kStagedPerCu);
         const int n_nq = grid - n_place;
         if (n_nq >= device_cu_count() && T > n_nq) {
             if (mode == kPlaceScanned) {
