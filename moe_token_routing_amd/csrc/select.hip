@@ -298,8 +298,13 @@ __device__ __forceinline__ void count_pick(int32_t* __restrict__ hist, int hist_
 }
 
 // EPL consecutive floats at p (16-byte vector loads when `vec`, which the
-// caller sets when the row length keeps them aligned).
-template <int EPL, bool FULL>
+// caller sets when the row length keeps them aligned). NT: the full-lane
+// 16-byte loads non-temporal (data read once, the projection's split-K
+// partials), so that they do not crowd the caches ahead of the next
+// kernel's reads: at 8192 tokens the route + dispatch + norm + quant call
+// 147.4 -> 143.0 us and the step 365.4 -> 359.8 us (three alternating runs).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <int EPL, bool FULL, bool NT = false>
 __device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, int n, float (&v)[EPL]) {
     if constexpr (FULL) {
         // every lane owns EPL experts and rows are 16-byte aligned: plain
@@ -307,7 +312,11 @@ __device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, 
         if constexpr (EPL % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < EPL; i += 4) {
-                const float4 q = *reinterpret_cast<const float4*>(p + i);
+                f32x4_t q;
+                if constexpr (NT)
+                    q = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + i));
+                else
+                    q = *reinterpret_cast<const f32x4_t*>(p + i);
                 v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
             }
         } else {
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
         if (logits_in) {
             load_run<EPL, FULL>(logits + row, vec, n, lg);
         } else {
-            load_run<EPL, FULL>(partials + s0 * plane + row, vec, n, lg);
+            load_run<EPL, FULL, true>(partials + s0 * plane + row, vec, n, lg);
             // a batch of splits is loaded before any is added (the loads
             // overlap); the sum still runs over the splits in order
 #pragma unroll 1
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(kSelectBlock) void select_reg_kernel(
 #pragma unroll
                 for (int u = 0; u < BATCH; ++u) {
                     if (p0 + u < s1) {
-                        load_run<EPL, FULL>(partials + (p0 + u) * plane + row, vec, n, q[u]);
+                        load_run<EPL, FULL, true>(partials + (p0 + u) * plane + row, vec, n, q[u]);
                     } else {
 #pragma unroll
                         for (int i = 0; i < EPL; ++i) q[u][i] = 0.f;
