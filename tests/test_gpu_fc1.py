@@ -70,6 +70,10 @@ def _case(T, k, E, K, N, seed, invalid=0.0, skew=None):
     (40, 2, 3, 576, 384, 0.0, None),            # 9 K stages: a second scale chunk of one stage
     (33, 3, 5, 1088, 256, 0.05, None),          # 17 K stages: a third chunk, a partial scale row
     (9, 2, 2, 16384, 128, 0.0, None),           # the largest K: 256 stages, 32 scale chunks
+    # from 1024 routed rows an expert the 256-row tiles (above: 128 x 128)
+    (1100, 2, 2, 128, 384, 0.0, None),          # 256 x 192
+    (1100, 2, 2, 128, 256, 0.02, None),         # 256 x 256
+    (1100, 2, 2, 128, 128, 0.0, [3, 1]),        # 256 x 128, uneven experts
 ])
 def test_fc1_small(T, k, E, K, N, invalid, skew):
     args = _case(T, k, E, K, N, seed=T + E, invalid=invalid, skew=skew)
@@ -171,10 +175,14 @@ def _case_swiglu(T, k, E, K, N, seed, invalid=0.0, skew=None):
 
 @pytest.mark.parametrize("T,k,E,K,N,invalid,skew", [
     (37, 3, 5, 128, 64, 0.1, None),             # 128 weight rows per tile (64 columns), ragged, invalid slots
-    (300, 2, 4, 64, 128, 0.0, [10, 0, 1, 3]),   # 256-row tiles, an empty expert, one over several tiles
-    (64, 4, 16, 256, 192, 0.0, None),           # 192-row tiles (96 columns), many small experts
-    (40, 2, 3, 576, 320, 0.0, None),            # 128-row tiles over 640 rows, 9 K stages
+    (300, 2, 4, 64, 128, 0.0, [10, 0, 1, 3]),   # an empty expert, one over several row tiles
+    (64, 4, 16, 256, 192, 0.0, None),           # many small experts
+    (40, 2, 3, 576, 320, 0.0, None),            # five 128-row tiles over 640 weight rows, 9 K stages
     (33, 3, 5, 1088, 384, 0.05, None),          # 17 K stages, a partial scale row
+    # from 1024 routed rows an expert the 256-row tiles (above: 128 x 128)
+    (1100, 2, 2, 128, 192, 0.0, None),          # 256 x 192 (384 weight rows, 96 columns a tile)
+    (1100, 2, 2, 128, 128, 0.02, None),         # 256 x 256 (128 columns)
+    (1100, 2, 2, 128, 64, 0.0, [3, 1]),         # 256 x 128 (64 columns), uneven experts
 ])
 def test_fc1_swiglu_small(T, k, E, K, N, invalid, skew):
     args = _case_swiglu(T, k, E, K, N, seed=T + E + 1, invalid=invalid, skew=skew)
