@@ -199,8 +199,8 @@ int moe_route_dispatch(const void* hidden, int hidden_dtype, const float* W, con
  * quantisation run beside the routing (on an auxiliary stream there). Here
  * the dispatch's place step and the norm + quant share one launch, blocks of
  * each side by side, when x's rows fill a wave or whole 256-thread blocks
- * (Hq / 16 = 64, 256, 512, 768 or 1024); otherwise they run one after the
- * other. Same outputs either way:
+ * (Hq / 16 = 64, 256, 512, 768 or 1024) or every slot lies in one dispatch
+ * tile; otherwise they run one after the other. Same outputs either way:
  * every output is bit-identical to moe_route_dispatch followed by
  * moe_norm_quant_nvfp4.
  *

@@ -413,26 +413,30 @@ __global__ __launch_bounds__(kRowBlock) void norm_quant_staged_kernel(
 // bandwidth-bound norm + quant instead of before it, with no second stream
 // to fork and join (TensorRT-LLM PR #21356, "Where they plug in": the
 // expert input prepared beside the routing).
-// ONE_TPT = 0: the staged norm + quant (one token per block, each block
-// visiting several); ONE_TPT = kWave or kRowBlock: the one-pass form, for
-// batches with fewer tokens than the launch has blocks (small batches).
-template <int MODE, int BPT, int ONE_TPT = 0>
+// NQ = kStagedNq: the staged norm + quant (one token per block, each block
+// visiting several); NQ = kWave or kRowBlock: the one-pass form, for batches
+// with fewer tokens than the launch has blocks (small batches); NQ = 0: the
+// one-pass form for rows that fill neither (`tpt` threads a token, bounds
+// checked).
+constexpr int kStagedNq = -1;
+
+template <int MODE, int BPT, int NQ = kStagedNq>
 __global__ __launch_bounds__(kRowBlock) void place_norm_quant_kernel(
     int n_place, const int32_t* __restrict__ ids, int n, int E, int tile, int tiles,
     const int32_t* __restrict__ tile_hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ dest, const u32x4* __restrict__ x,
     const float* __restrict__ norm_w, float gain_center, float eps, const float* __restrict__ global_scale,
-    int T, int H, uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
+    int T, int H, int tpt, uint2* __restrict__ packed, uint8_t* __restrict__ scales) {
     static_assert(kDispBlock == kRowBlock, "one block size");
     extern __shared__ __attribute__((aligned(16))) int32_t place_lds[];
     if (static_cast<int>(blockIdx.x) < n_place)
         place_body<MODE>(blockIdx.x, place_lds, ids, n, E, tile, tiles, tile_hist, counts, offsets, perm, dest);
-    else if constexpr (ONE_TPT == 0)
+    else if constexpr (NQ == kStagedNq)
         norm_quant_staged_body<BPT, kRowBlock>(blockIdx.x - n_place, gridDim.x - n_place, x, norm_w, gain_center,
                                                eps, global_scale, T, H, H / 8, packed, scales);
     else
-        norm_quant_body<BPT, ONE_TPT>(blockIdx.x - n_place, gridDim.x - n_place, x, norm_w, gain_center, eps,
-                                      global_scale, T, H, H / 8, ONE_TPT, packed, scales);
+        norm_quant_body<BPT, NQ>(blockIdx.x - n_place, gridDim.x - n_place, x, norm_w, gain_center, eps,
+                                 global_scale, T, H, H / 8, NQ == 0 ? tpt : NQ, packed, scales);
 }
 
 struct BlockGeom {
@@ -495,15 +499,15 @@ int check_norm_quant(const uint16_t* x, const float* norm_w, float gain_center, 
 
 namespace {
 
-template <int MODE, int BPT, int ONE_TPT = 0>
+template <int MODE, int BPT, int NQ = kStagedNq>
 int launch_place_norm_quant(int grid, int n_place, size_t lds, const int32_t* topk_ids, int n, int E, int tile,
                             int tiles, int32_t* tile_counts, int32_t* counts, int32_t* offsets, int32_t* perm,
                             int32_t* dest, const uint16_t* x, const float* norm_w, float gain_center, float eps,
-                            const float* global_scale, int T, int H, uint8_t* packed, uint8_t* scales,
+                            const float* global_scale, int T, int H, int tpt, uint8_t* packed, uint8_t* scales,
                             void* stream) {
-    return launch(place_norm_quant_kernel<MODE, BPT, ONE_TPT>, dim3(grid), dim3(kRowBlock), lds, stream, n_place, topk_ids,
+    return launch(place_norm_quant_kernel<MODE, BPT, NQ>, dim3(grid), dim3(kRowBlock), lds, stream, n_place, topk_ids,
                   n, E, tile, tiles, static_cast<const int32_t*>(tile_counts), counts, offsets, perm, dest,
-                  reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H,
+                  reinterpret_cast<const u32x4*>(x), norm_w, gain_center, eps, global_scale, T, H, tpt,
                   reinterpret_cast<uint2*>(packed), scales);
 }
 
@@ -560,7 +564,7 @@ int run_place_norm_quant(const int32_t* topk_ids, long long n, int E, int32_t* c
     if (mode == M && geo.bpt == B)                                                                            \
         return launch_place_norm_quant<M, B>(grid, n_place, lds, topk_ids, static_cast<int>(n), E, d.tile, d.tiles, \
                                              tile_counts, counts, offsets, perm, dest, x, norm_w, gain_center, eps, \
-                                             global_scale, T, H, packed, scales, stream);
+                                             global_scale, T, H, kRowBlock, packed, scales, stream);
             MOE_PNQ(kPlaceSingle, 1) MOE_PNQ(kPlaceSingle, 2) MOE_PNQ(kPlaceSingle, 3) MOE_PNQ(kPlaceSingle, 4)
             MOE_PNQ(kPlaceFused, 1) MOE_PNQ(kPlaceFused, 2) MOE_PNQ(kPlaceFused, 3) MOE_PNQ(kPlaceFused, 4)
             MOE_PNQ(kPlaceScanned, 1) MOE_PNQ(kPlaceScanned, 2) MOE_PNQ(kPlaceScanned, 3) MOE_PNQ(kPlaceScanned, 4)
@@ -594,14 +598,32 @@ int run_place_norm_quant(const int32_t* topk_ids, long long n, int E, int32_t* c
     if (mode == M && geo.bpt == B && one_tpt == TP)                                                             \
         return launch_place_norm_quant<M, B, TP>(n_place + n_nq, n_place, lds, topk_ids, static_cast<int>(n), E,  \
                                                  d.tile, d.tiles, tile_counts, counts, offsets, perm, dest, x,    \
-                                                 norm_w, gain_center, eps, global_scale, T, H, packed, scales,   \
-                                                 stream);
+                                                 norm_w, gain_center, eps, global_scale, T, H, TP, packed,       \
+                                                 scales, stream);
 #define MOE_PNQ1_MODE(M) \
     MOE_PNQ1(M, 1, kWave) MOE_PNQ1(M, 1, kRowBlock) MOE_PNQ1(M, 2, kRowBlock) MOE_PNQ1(M, 3, kRowBlock) \
     MOE_PNQ1(M, 4, kRowBlock)
         MOE_PNQ1_MODE(kPlaceSingle) MOE_PNQ1_MODE(kPlaceFused) MOE_PNQ1_MODE(kPlaceScanned)
 #undef MOE_PNQ1_MODE
 #undef MOE_PNQ1
+    }
+    // Rows that fill neither a wave nor a block (fewer than 1024 or not a
+    // multiple of 1024 wide), with every slot in one dispatch tile (small
+    // batches): the generic one-pass form beside the single place block.
+    if (n > 0 && T > 0 && geo.bpt <= 4 && place_mode(n, E) == kPlaceSingle) {
+        const DispatchTiles d = dispatch_tiles(n);
+        const size_t lds = place_lds_bytes(kPlaceSingle, E);
+        const int needed = ceil_div(T, kRowBlock / geo.tpt);
+        const int cap = device_cu_count() * 4;
+        const int n_nq = needed < cap ? needed : cap;
+#define MOE_PNQ0(B)                                                                                             \
+    if (geo.bpt == B)                                                                                           \
+        return launch_place_norm_quant<kPlaceSingle, B, 0>(1 + n_nq, 1, lds, topk_ids, static_cast<int>(n), E,   \
+                                                           d.tile, d.tiles, tile_counts, counts, offsets, perm,  \
+                                                           dest, x, norm_w, gain_center, eps, global_scale, T,   \
+                                                           H, geo.tpt, packed, scales, stream);
+        MOE_PNQ0(1) MOE_PNQ0(2) MOE_PNQ0(3) MOE_PNQ0(4)
+#undef MOE_PNQ0
     }
     int rc = n > 0 ? run_place(topk_ids, n, E, counts, offsets, perm, dest, tile_counts, stream)
                    : run_dispatch_empty(counts, offsets, E, stream);
