@@ -16,8 +16,9 @@
 // slot order (one FMA per element). That is about six VALU operations per
 // element, so the kernel stays under the HBM time. The per-element gain is
 // staged in LDS once per block and read there for every token the block
-// visits (grid-stride loop). With no more tokens than CUs, one 1024-thread
-// block serves each token.
+// visits (grid-stride loop). Batches of no more tokens than CUs take
+// combine_token_kernel: one 1024-thread block per token, or per part of a
+// token's row when CUs are left over.
 #include <cmath>
 
 #include "launch.hpp"
@@ -37,22 +38,13 @@ struct CombineCfg {
 // and every thread owns exactly VPT vectors (H / 8 = VPT TPT). The token,
 // its slots and their validity are then the same for the whole wave, so they
 // live in scalar registers and the per-vector bounds checks disappear.
-// BLOCK = kBigBlock (TPT = BLOCK): one token per 1024-thread block, for
-// batches with no more tokens than CUs. A token then has a whole CU, four
-// waves per SIMD, each thread a quarter of the vectors and so a quarter of
-// the per-element work (a wave64 VALU operation holds a SIMD four cycles),
-// and with one vector a thread all k rows load in one group.
-constexpr int kBigBlock = 1024;
-
-template <int VPT, int TPT, int BLOCK = kRowBlock>
-__global__ __launch_bounds__(BLOCK) void combine_kernel(
+template <int VPT, int TPT>
+__global__ __launch_bounds__(kRowBlock) void combine_kernel(
     const u32x4* __restrict__ expert_out, int R, const int32_t* __restrict__ slots,
     const float* __restrict__ topk_w, const float* __restrict__ norm_w, float gain_center,
     float eps, int T, int H, int k, int tpt, u32x4* __restrict__ out) {
-    static_assert(BLOCK == kRowBlock || TPT == BLOCK, "the big block serves one token");
-    // (the big block's 128 registers a thread hold four rows of a vector)
-    constexpr int G = BLOCK == kRowBlock ? CombineCfg<VPT>::G : (VPT == 1 ? 4 : 2);
-    __shared__ float red[(BLOCK / kWave) * G];
+    constexpr int G = CombineCfg<VPT>::G;
+    __shared__ float red[(kRowBlock / kWave) * G];
     // gain = gain_center + norm_w, staged once per block. Vector v's eight
     // values live as gain_lo[v] (elements 0-3) and gain_hi[v] (4-7), so a
     // wave's 16-byte LDS reads are consecutive.
@@ -60,7 +52,7 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(
     const int nvec = H >> 3;
     float4* gain_lo = gain_lds;
     float4* gain_hi = gain_lds + nvec;
-    for (int v = threadIdx.x; v < nvec; v += BLOCK) {
+    for (int v = threadIdx.x; v < nvec; v += kRowBlock) {
         const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
         const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
         gain_lo[v] = make_float4(gain_center + a.x, gain_center + a.y, gain_center + a.z, gain_center + a.w);
@@ -70,7 +62,7 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(
 
     constexpr bool WHOLE = TPT != 0;
     if (WHOLE) tpt = TPT;
-    const int tokens_per_block = BLOCK / tpt;
+    const int tokens_per_block = kRowBlock / tpt;
     // with TPT a multiple of the wave, a wave's lanes share one token
     const int sub = WHOLE ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / TPT)
                           : static_cast<int>(threadIdx.x) / tpt;
@@ -167,16 +159,169 @@ __global__ __launch_bounds__(BLOCK) void combine_kernel(
     }
 }
 
-template <int VPT, int TPT, int BLOCK = kRowBlock>
+// Batches of no more tokens than CUs, rows of 1024 * VPT vectors: one
+// 1024-thread block per token, or S blocks (S = 1, 2 or 4) when CUs are left
+// over. Each of the S blocks reads the token's whole rows for the sums of
+// squares, but only its S-th of the waves (part `part`) normalises, weights
+// and stores, so the per-element work (most of the time at these sizes)
+// spreads over S CUs. Block b serves token (b / 8 / S) * 8 + b % 8: the S
+// blocks of a token share b % 8 and so an XCD (blocks go to the 8 XCDs in
+// turn) and its L2, which serves the repeated row reads.
+// Each thread owns VPT vectors, so its gains stay in registers (no LDS stage
+// and no barrier before the first row load); lane j of every wave holds pick
+// j's slot and weight (k <= 32), so one load brings them all and the first
+// rows issue right behind it; the next group's rows are in flight while the
+// block adds the current group's sums of squares, and two reduction buffers
+// alternate, so a group costs one barrier. The arithmetic and its order are
+// those of combine_kernel.
+constexpr int kBigBlock = 1024;
+constexpr int kXcds = 8;
+constexpr int kMaxParts = 4;
+
+template <int VPT>
+__global__ __launch_bounds__(kBigBlock) void combine_token_kernel(
+    const u32x4* __restrict__ expert_out, int R, const int32_t* __restrict__ slots,
+    const float* __restrict__ topk_w, const float* __restrict__ norm_w, float gain_center,
+    float eps, int T, int H, int k, int S, u32x4* __restrict__ out) {
+    constexpr int G = VPT == 1 ? 8 : 4;   // rows a group: 32 data VGPRs, twice for the next group
+    constexpr int kWaves = kBigBlock / kWave;
+    __shared__ float red[2][kWaves][G];
+    const int round = blockIdx.x / kXcds;
+    const int t = (round / S) * kXcds + blockIdx.x % kXcds;
+    const int part = round % S;
+    if (t >= T) return;
+    const int nvec = H >> 3;
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    const bool mine = wave / (kWaves / S) == part;   // this wave's vectors are this block's to write
+    int pick_r = -1;
+    float pick_w = 0.f;
+    if (lane < k) {
+        pick_r = slots[static_cast<size_t>(t) * k + lane];
+        pick_w = topk_w[static_cast<size_t>(t) * k + lane];
+    }
+    float gv[VPT][8] = {};
+    if (mine) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = threadIdx.x + i * kBigBlock;
+            const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
+            const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
+            gv[i][0] = gain_center + a.x; gv[i][1] = gain_center + a.y;
+            gv[i][2] = gain_center + a.z; gv[i][3] = gain_center + a.w;
+            gv[i][4] = gain_center + b.x; gv[i][5] = gain_center + b.y;
+            gv[i][6] = gain_center + b.z; gv[i][7] = gain_center + b.w;
+        }
+    }
+    float acc[VPT][8];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+
+    // rows of picks j0 .. j0 + G - 1; every lane read happens outside the
+    // branches (lanes k .. 63 hold slot -1, and j0 + G - 1 < 64 since k <= 32),
+    // so the wait for the picks is taken once and the row loads all stay in
+    // flight together
+    auto issue = [&](u32x4 (&x)[G][VPT], bool (&ok)[G], int j0) {
+        int r[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) r[g] = __builtin_amdgcn_readlane(pick_r, j0 + g);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            ok[g] = r[g] >= 0 && r[g] < R;
+            if (ok[g]) {
+                const u32x4* row = expert_out + static_cast<size_t>(r[g]) * nvec;
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) x[g][i] = load_nt(&row[threadIdx.x + i * kBigBlock]);
+            }
+        }
+    };
+    u32x4 x[G][VPT];
+    bool ok[G];
+    issue(x, ok, 0);
+    int buf = 0;
+    for (int j0 = 0; j0 < k; j0 += G, buf ^= 1) {
+        u32x4 xn[G][VPT];
+        bool okn[G];
+        issue(xn, okn, j0 + G);
+        float wt[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) wt[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pick_w), j0 + g));
+        float ss[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float s = 0.f;
+            if (ok[g]) {
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    s = dot2_sq(x[g][i].x, s);
+                    s = dot2_sq(x[g][i].y, s);
+                    s = dot2_sq(x[g][i].z, s);
+                    s = dot2_sq(x[g][i].w, s);
+                }
+            }
+            ss[g] = wave_sum(s);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) red[buf][wave][g] = ss[g];
+        }
+        __syncthreads();
+        // lane g of each wave adds pick j0 + g's wave sums (in wave order)
+        // and takes its 1 / rms once; the wave reads the G results back
+        float rv = 0.f;
+        if (mine && lane < G) {
+            float s = red[buf][0][lane];
+            for (int w = 1; w < kWaves; ++w) s += red[buf][w][lane];
+            rv = 1.0f / sqrtf(s / static_cast<float>(H) + eps);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (!ok[g] || !mine) continue;
+            const float rinv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), g));
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float y0 = (bf16_lo(w4[q]) * gv[i][2 * q]) * rinv;
+                    const float y1 = (bf16_hi(w4[q]) * gv[i][2 * q + 1]) * rinv;
+                    const uint32_t z = cvt_pk_bf16(y0, y1);
+                    acc[i][2 * q] = __builtin_fmaf(wt[g], bf16_lo(z), acc[i][2 * q]);
+                    acc[i][2 * q + 1] = __builtin_fmaf(wt[g], bf16_hi(z), acc[i][2 * q + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            ok[g] = okn[g];
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) x[g][i] = xn[g][i];
+        }
+    }
+    if (!mine) return;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        u32x4 o;
+        o.x = cvt_pk_bf16(acc[i][0], acc[i][1]);
+        o.y = cvt_pk_bf16(acc[i][2], acc[i][3]);
+        o.z = cvt_pk_bf16(acc[i][4], acc[i][5]);
+        o.w = cvt_pk_bf16(acc[i][6], acc[i][7]);
+        store_nt(o, &out[static_cast<size_t>(t) * nvec + threadIdx.x + i * kBigBlock]);
+    }
+}
+
+template <int VPT, int TPT>
 int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
                    const float* norm_w, float gain_center, float eps, int T, int H, int k,
                    const RowGeom& geo, uint16_t* out, void* stream) {
-    const int tokens_per_block = BLOCK / geo.tpt;
+    const int tokens_per_block = kRowBlock / geo.tpt;
     const int needed = ceil_div(T, tokens_per_block);
     const size_t lds = sizeof(float) * static_cast<size_t>(H);
-    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT, TPT, BLOCK>, BLOCK, lds);
+    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT, TPT>, kRowBlock, lds);
     const int grid = needed < cap ? needed : cap;
-    return launch(combine_kernel<VPT, TPT, BLOCK>, dim3(grid), dim3(BLOCK), lds, stream,
+    return launch(combine_kernel<VPT, TPT>, dim3(grid), dim3(kRowBlock), lds, stream,
                   reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
                   gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
 }
@@ -198,16 +343,17 @@ extern "C" int moe_combine(const uint16_t* expert_out, int R, const int32_t* slo
     if (!slots || !topk_w || !norm_w || !out || (R > 0 && !expert_out)) return MOE_ERR_NULL_ARG;
     if (!all_aligned16(expert_out, slots, topk_w, norm_w, out)) return MOE_ERR_ALIGN;
     RowGeom geo = row_geom(H);
-    // no more tokens than CUs and rows of whole 1024-vector multiples: one
-    // 1024-thread block per token (at 128 tokens of 8192: 16.2 -> 13.8 us)
-    if (T <= device_cu_count() && geo.nvec % kBigBlock == 0 && geo.nvec / kBigBlock <= 2) {
-        geo.tpt = kBigBlock;
-        geo.vpt = geo.nvec / kBigBlock;
-        if (geo.vpt == 1)
-            return launch_combine<1, kBigBlock, kBigBlock>(expert_out, R, slots, topk_w, norm_w, gain_center, eps,
-                                                          T, H, k, geo, out, stream);
-        return launch_combine<2, kBigBlock, kBigBlock>(expert_out, R, slots, topk_w, norm_w, gain_center, eps, T,
-                                                      H, k, geo, out, stream);
+    // no more tokens than CUs and rows of 1024 or 2048 vectors: the token
+    // kernel, its row cut in S parts while CUs are left over (at 128 tokens
+    // of 8192, k 8: 10.7 -> 7.2 us; at 5 tokens, k 32: 37.7 -> 15.4 us)
+    const int cus = device_cu_count();
+    if (T <= cus && (geo.nvec == kBigBlock || geo.nvec == 2 * kBigBlock)) {
+        const int T8 = ceil_div(T, kXcds) * kXcds;
+        int S = 1;
+        while (S < kMaxParts && T8 * S * 2 <= cus) S *= 2;
+        auto kern = geo.nvec == kBigBlock ? combine_token_kernel<1> : combine_token_kernel<2>;
+        return launch(kern, dim3(T8 * S), dim3(kBigBlock), 0, stream, reinterpret_cast<const u32x4*>(expert_out),
+                      R, slots, topk_w, norm_w, gain_center, eps, T, H, k, S, reinterpret_cast<u32x4*>(out));
     }
     // rows of at most 128 vectors (H <= 1024): one wave per token, so the
     // token's sums of squares never meet in LDS (measured at H 1024, k 22:

@@ -135,12 +135,15 @@ def test_combine_empty_and_zero_rows():
     assert out.shape == (0, 64)
 
 
-@pytest.mark.parametrize("T,k,H", [(1, 1, 8192), (5, 32, 8192), (3, 7, 16384), (256, 8, 8192), (300, 8, 8192)])
+@pytest.mark.parametrize("T,k,H", [(1, 1, 8192), (5, 32, 8192), (3, 7, 16384), (100, 8, 8192), (37, 5, 16384),
+                                   (128, 8, 8192), (256, 8, 8192), (300, 8, 8192)])
 def test_combine_one_token_per_cu(T, k, H):
-    """Batches of no more tokens than CUs at widths of whole 1024-vector
-    multiples take one 1024-thread block per token (300 tokens: the
-    256-thread blocks, beside it): k off the four-row groups, a whole token
-    invalid, out-of-range slots, and power-of-two rows exact with eps = 0."""
+    """Batches of no more tokens than CUs at 8192 or 16384 wide rows take one
+    1024-thread block per token, or per half or quarter of a row while CUs
+    are left over (four parts up to 64 tokens, two up to 128, one above; 300
+    tokens: the 256-thread blocks, beside it): token counts off the
+    multiples of 8, k off the row groups, a whole token invalid, out-of-range
+    slots, and power-of-two rows exact with eps = 0."""
     g = np.random.default_rng(T * k + H)
     R = T * k + 5
     eo = wl.f32_to_bf16_bits((g.standard_normal((R, H)) * 3).astype(np.float32))
