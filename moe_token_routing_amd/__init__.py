@@ -89,15 +89,38 @@ def _check(fn: str, status: int):
         raise MoeError(fn, status)
 
 
+# The checks and conversions below run on every call, so they take the
+# cheapest route to the same facts (a decode-sized call's own host work is a
+# few microseconds; these helpers had cost about twice that).
+
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for the c_void_p parameter
+    return None if t is None else t.data_ptr()
+
+
+try:
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:   # older torch: the public query (slower)
+    def _raw_stream(index):
+        return torch.cuda.current_stream(index).cuda_stream
 
 
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The device's current HIP stream, as a raw handle."""
+    return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
 
 
 def _need(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
+    try:
+        if (t.is_cuda and t.dtype in dtypes and t.is_contiguous() and (shape is None or t.shape == tuple(shape))
+                and (device is None or t.device == device)):
+            return
+    except AttributeError:
+        pass
+    _need_failed(t, name, dtypes, shape, device)
+
+
+def _need_failed(t, name, dtypes, shape, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a tensor" % name)
     if t.device.type != "cuda":
@@ -110,6 +133,7 @@ def _need(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
         raise ValueError("%s must be contiguous" % name)
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    raise AssertionError("%s failed a check that names no reason" % name)
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
