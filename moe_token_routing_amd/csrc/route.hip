@@ -49,7 +49,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kTargetBlocks = 480;   // about two blocks per CU
+constexpr int kTargetBlocks = 480;        // about two blocks per CU
+constexpr int kTargetBlocksSmall = 256;   // one block per CU (batches of up to 256 tokens)
 constexpr int kPipeTargetBlocks = 256;   // one block per CU (proj_pipe_kernel)
 #ifndef MOE_PIPE_SPLIT_IN_REGS
 #define MOE_PIPE_SPLIT_IN_REGS 1
@@ -555,8 +556,13 @@ inline RoutePlan plan_route(int T, int H, int E, int hidden_dtype) {
     p.tiles_n = ceil_div(E, 128 * p.nt);
     const int tiles = p.tiles_m * p.tiles_n;
     const int chunks = ceil_div(H, kKC);
+    // split K until about two blocks a CU; small batches stop at one a CU,
+    // whose blocks then run twice the K-steps against half the partials
+    // (at 128 tokens of 8192 x 256: split 64 -> 32, projection 10.6 -> 10.1
+    // us, selection 6.2 -> 5.2 us; split 16 took 14 us)
+    const int target = T <= 256 ? kTargetBlocksSmall : kTargetBlocks;
     int ns = 1;
-    while (tiles * ns < kTargetBlocks && ns * 2 <= chunks && ns < 64) ns *= 2;
+    while (tiles * ns < target && ns * 2 <= chunks && ns < 64) ns *= 2;
     const int per = ceil_div(chunks, ns);   // K stages per split
     p.kslice = per * kKC;
     p.nsplit = ceil_div(H, p.kslice);
