@@ -16,7 +16,8 @@
 // slot order (one FMA per element). That is about six VALU operations per
 // element, so the kernel stays under the HBM time. The per-element gain is
 // staged in LDS once per block and read there for every token the block
-// visits (grid-stride loop). Batches of no more tokens than CUs take
+// visits; the grid has one block per block's worth of tokens, so the
+// hardware hands out tokens as blocks finish. Batches of no more tokens than CUs take
 // combine_token_kernel: one 1024-thread block per token, or per part of a
 // token's row when CUs are left over.
 #include <cmath>
@@ -316,11 +317,14 @@ template <int VPT, int TPT>
 int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, const float* topk_w,
                    const float* norm_w, float gain_center, float eps, int T, int H, int k,
                    const RowGeom& geo, uint16_t* out, void* stream) {
+    // One block for each block's worth of tokens, dispatched by the hardware
+    // as blocks finish, rather than a resident grid striding over the
+    // tokens: at 8192 tokens of 8192, k 8 the combine 213 -> 203 us, at
+    // 32768 tokens of 1024, k 22 298 -> 275 us (the gain staging per block
+    // reads the gain from L2); the kernel's token loop still covers any grid.
     const int tokens_per_block = kRowBlock / geo.tpt;
-    const int needed = ceil_div(T, tokens_per_block);
+    const int grid = ceil_div(T, tokens_per_block);
     const size_t lds = sizeof(float) * static_cast<size_t>(H);
-    const int cap = device_cu_count() * resident_blocks(combine_kernel<VPT, TPT>, kRowBlock, lds);
-    const int grid = needed < cap ? needed : cap;
     return launch(combine_kernel<VPT, TPT>, dim3(grid), dim3(kRowBlock), lds, stream,
                   reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
                   gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
