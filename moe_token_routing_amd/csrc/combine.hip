@@ -15,9 +15,10 @@
 // (v_cvt_pk_bf16_f32) and the weighted rows accumulate in FP32 registers in
 // slot order (one FMA per element). That is about six VALU operations per
 // element, so the kernel stays under the HBM time. The per-element gain is
-// staged in LDS once per block and read there for every token the block
-// visits; the grid has one block per block's worth of tokens, so the
-// hardware hands out tokens as blocks finish. Batches of no more tokens than CUs take
+// kept in registers when a token fills the block, else staged in LDS once
+// per block and read there for every token the block visits; the grid has
+// one block per block's worth of tokens, so the hardware hands out tokens
+// as blocks finish. Batches of no more tokens than CUs take
 // combine_token_kernel: one 1024-thread block per token, or per part of a
 // token's row when CUs are left over.
 #include <cmath>
@@ -46,20 +47,43 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     float eps, int T, int H, int k, int tpt, u32x4* __restrict__ out) {
     constexpr int G = CombineCfg<VPT>::G;
     __shared__ float red[(kRowBlock / kWave) * G];
-    // gain = gain_center + norm_w, staged once per block. Vector v's eight
-    // values live as gain_lo[v] (elements 0-3) and gain_hi[v] (4-7), so a
-    // wave's 16-byte LDS reads are consecutive.
+    // gain = gain_center + norm_w. When a token fills the block (TPT =
+    // kRowBlock) and a thread owns at most four vectors, each thread keeps
+    // the gains of its own VPT vectors in registers, read once (the block has one token: staging the whole gain
+    // row in LDS and reading it back per row had cost the prefill combine
+    // 203 against 198 us). Otherwise it is staged once per block: vector v's
+    // eight values live as gain_lo[v] (elements 0-3) and gain_hi[v] (4-7), so
+    // a wave's 16-byte LDS reads are consecutive.
+    constexpr bool GREG = TPT == kRowBlock && VPT <= 4;
+    float greg[GREG ? VPT : 1][8];
+    if constexpr (GREG) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = static_cast<int>(threadIdx.x) + i * kRowBlock;
+            const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
+            const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
+            greg[i][0] = gain_center + a.x;
+            greg[i][1] = gain_center + a.y;
+            greg[i][2] = gain_center + a.z;
+            greg[i][3] = gain_center + a.w;
+            greg[i][4] = gain_center + b.x;
+            greg[i][5] = gain_center + b.y;
+            greg[i][6] = gain_center + b.z;
+            greg[i][7] = gain_center + b.w;
+        }
+    }
     extern __shared__ float4 gain_lds[];
     const int nvec = H >> 3;
     float4* gain_lo = gain_lds;
     float4* gain_hi = gain_lds + nvec;
+    if (!GREG)
     for (int v = threadIdx.x; v < nvec; v += kRowBlock) {
         const float4 a = reinterpret_cast<const float4*>(norm_w)[2 * v];
         const float4 b = reinterpret_cast<const float4*>(norm_w)[2 * v + 1];
         gain_lo[v] = make_float4(gain_center + a.x, gain_center + a.y, gain_center + a.z, gain_center + a.w);
         gain_hi[v] = make_float4(gain_center + b.x, gain_center + b.y, gain_center + b.z, gain_center + b.w);
     }
-    __syncthreads();
+    if (!GREG) __syncthreads();
 
     constexpr bool WHOLE = TPT != 0;
     if (WHOLE) tpt = TPT;
@@ -130,8 +154,21 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
                     const int v = tid + i * tpt;
                     if (!WHOLE && v >= nvec) continue;
                     const uint32_t w4[4] = {x[g][i].x, x[g][i].y, x[g][i].z, x[g][i].w};
-                    const float4 ga = gain_lo[v], gb = gain_hi[v];
-                    const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+                    float gv[8];
+                    if constexpr (GREG) {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) gv[q] = greg[i][q];
+                    } else {
+                        const float4 ga = gain_lo[v], gb = gain_hi[v];
+                        gv[0] = ga.x;
+                        gv[1] = ga.y;
+                        gv[2] = ga.z;
+                        gv[3] = ga.w;
+                        gv[4] = gb.x;
+                        gv[5] = gb.y;
+                        gv[6] = gb.z;
+                        gv[7] = gb.w;
+                    }
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float y0 = (bf16_lo(w4[q]) * gv[2 * q]) * rinv;
@@ -324,7 +361,8 @@ int launch_combine(const uint16_t* expert_out, int R, const int32_t* slots, cons
     // reads the gain from L2); the kernel's token loop still covers any grid.
     const int tokens_per_block = kRowBlock / geo.tpt;
     const int grid = ceil_div(T, tokens_per_block);
-    const size_t lds = sizeof(float) * static_cast<size_t>(H);
+    // the gain row in LDS, unless the kernel keeps the gains in registers
+    const size_t lds = TPT == kRowBlock && VPT <= 4 ? 0 : sizeof(float) * static_cast<size_t>(H);
     return launch(combine_kernel<VPT, TPT>, dim3(grid), dim3(kRowBlock), lds, stream,
                   reinterpret_cast<const u32x4*>(expert_out), R, slots, topk_w, norm_w,
                   gain_center, eps, T, H, k, geo.tpt, reinterpret_cast<u32x4*>(out));
