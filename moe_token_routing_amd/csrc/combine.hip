@@ -94,8 +94,11 @@ __global__ __launch_bounds__(kRowBlock) void combine_kernel(
     const int tid = static_cast<int>(threadIdx.x) - sub * tpt;
     const float hf = static_cast<float>(H);
 
-    for (int t0 = blockIdx.x * tokens_per_block; t0 < T; t0 += gridDim.x * tokens_per_block) {
-        const int t = t0 + sub;
+    // 64-bit token index: with a block per token the stride is the whole
+    // batch, and t0 + stride must not overflow for batches past 2^30 tokens
+    const long long stride = static_cast<long long>(gridDim.x) * tokens_per_block;
+    for (long long t0 = static_cast<long long>(blockIdx.x) * tokens_per_block; t0 < T; t0 += stride) {
+        const int t = static_cast<int>(t0) + sub;
         const bool tok_ok = t < T;
         float acc[VPT][8];
 #pragma unroll
